@@ -1,0 +1,268 @@
+"""Pins that tie the CPU oracle to something other than itself.
+
+Each ``pin_*`` function takes a loaded oracle library and raises
+AssertionError when the oracle disagrees with:
+
+* a pure-Python brute force that uses the *sorted-row* definition of the
+  row top-2 (max, lowest argmax, second element of the row sorted in
+  descending order with multiplicity), independent of the oracle's scan;
+* NumPy's int64 matrix product (a library routine) for the scores;
+* closed forms (all-255 rows, zero rows, one-hot descriptors);
+* hand-derived fixtures under ``tests/golden/``, each citing the statement
+  of the SERAC README it encodes;
+* the gate's closed cases (angles of 0 and pi/2, ties, one column);
+* planted-correspondence recovery on seeded synthetic pairs.
+
+The functions are shared by ``test_oracle_pins.py`` (the real oracle must
+pass them all) and ``test_oracle_mutants.py`` (every plausible mistake
+planted in a copy of the oracle must fail at least one of them).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle
+from sift_descriptor_nearest_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+NORM2 = 512 * 512
+
+
+# ---------------------------------------------------------------- brute force
+def brute_top2(A: np.ndarray, B: np.ndarray):
+    """Row top-2 and column best from the sorted-row / argmax definitions."""
+    nA, nB = len(A), len(B)
+    S = [[sum(int(a) * int(b) for a, b in zip(A[i], B[j])) for j in range(nB)]
+         for i in range(nA)]
+    row = []
+    for i in range(nA):
+        srt = sorted(S[i], reverse=True)
+        best = srt[0] if nB else 0
+        second = srt[1] if nB >= 2 else 0
+        idx = S[i].index(best) if best > 0 else -1
+        row.append((best, idx, second))
+    col = []
+    for j in range(nB):
+        c = [S[i][j] for i in range(nA)]
+        best = max(c) if nA else 0
+        idx = c.index(best) if best > 0 else -1
+        col.append((best, idx))
+    return (np.array(row, dtype=np.int32).reshape(nA, 3),
+            np.array(col, dtype=np.int32).reshape(nB, 2))
+
+
+def py_angle(s: int) -> float:
+    return math.acos(1.0 if s >= NORM2 else s / NORM2)
+
+
+def brute_matches(row, col, max_ratio, max_distance, cross_check):
+    out = []
+    for i, (best, idx, second) in enumerate(row.tolist()):
+        if idx < 0:
+            continue
+        d1, d2 = py_angle(best), py_angle(second)
+        if not d1 <= max_distance:
+            continue
+        if not d1 < max_ratio * d2:
+            continue
+        if cross_check and col[idx][1] != i:
+            continue
+        out.append((i, idx))
+    return np.array(out, dtype=np.uint32).reshape(-1, 2)
+
+
+def tie_heavy(rng: np.random.Generator, n: int) -> np.ndarray:
+    """Descriptors with 1-3 nonzero bytes in {1, 2}, plus special rows."""
+    X = np.zeros((n, 128), dtype=np.uint8)
+    for r in range(n):
+        u = rng.random()
+        if u < 0.1:
+            continue                                  # all-zero row
+        if u < 0.15:
+            X[r] = 255                                # all-255 row
+            continue
+        if u < 0.3 and r > 0:
+            X[r] = X[rng.integers(0, r)]              # duplicate of an earlier row
+            continue
+        nz = rng.integers(1, 4)
+        pos = rng.choice(8, size=nz, replace=False)   # few dims -> many ties
+        X[r, pos] = rng.integers(1, 3, size=nz)
+    return X
+
+
+# ---------------------------------------------------------------------- pins
+def pin_brute_tiny(L):
+    """Oracle == pure-Python sorted-row brute force on tie-heavy tiny pairs."""
+    rng = np.random.default_rng(1234)
+    sizes = (0, 1, 2, 3, 17, 40)
+    for nA in sizes:
+        for nB in sizes:
+            A = tie_heavy(rng, nA)
+            B = tie_heavy(rng, nB)
+            row, col = brute_top2(A, B)
+            orow, ocol = oracle.top2(A, B, L=L)
+            assert np.array_equal(orow, row), ("row", nA, nB)
+            assert np.array_equal(ocol, col), ("col", nA, nB)
+            for r in (0.8, 1.0, 1.5):
+                for cc in (True, False):
+                    want = brute_matches(row, col, r, math.inf, cc)
+                    got = oracle.match_pair(A, B, r, math.inf, cc, L=L)
+                    assert np.array_equal(got, want), ("match", nA, nB, r, cc)
+
+
+def pin_numpy_scores(L):
+    """Top-2 / column best == sorted rows of NumPy's int64 A @ B.T."""
+    rng = np.random.default_rng(7)
+    for nA, nB in ((300, 517), (129, 1), (1, 260)):
+        A = synth.desc(rng, nA)
+        B = synth.desc(rng, nB)
+        if nB > 4:
+            B[3] = B[1]                    # a duplicated column -> top-1 tie
+        if nA > 6:
+            A[5] = A[2]                    # a duplicated row -> column tie
+            A[0] = 0                       # a zero row
+        S = A.astype(np.int64) @ B.astype(np.int64).T
+        srt = -np.sort(-S, axis=1)
+        best = srt[:, 0]
+        second = srt[:, 1] if nB >= 2 else np.zeros(nA, dtype=np.int64)
+        idx = np.where(best > 0, np.argmax(S, axis=1), -1)
+        cbest = S.max(axis=0)
+        cidx = np.where(cbest > 0, np.argmax(S, axis=0), -1)
+        orow, ocol = oracle.top2(A, B, L=L)
+        assert np.array_equal(orow[:, 0], best)
+        assert np.array_equal(orow[:, 1], idx)
+        assert np.array_equal(orow[:, 2], second)
+        assert np.array_equal(ocol[:, 0], cbest)
+        assert np.array_equal(ocol[:, 1], cidx)
+        # the sampled entry points agree with the full one
+        sel = np.arange(0, nA, 7, dtype=np.int32)
+        assert np.array_equal(oracle.rows(A, B, sel, L=L), orow[sel])
+        selc = np.arange(0, nB, 5, dtype=np.int32)
+        assert np.array_equal(oracle.cols(A, B, selc, L=L), ocol[selc])
+
+
+def pin_closed_forms(L):
+    """All-255 x all-255 = 128*255^2; all-255 x b = 255*sum(b); zeros -> -1."""
+    rng = np.random.default_rng(3)
+    B = synth.desc(rng, 5)
+    A = np.zeros((3, 128), dtype=np.uint8)
+    A[1] = 255
+    B2 = np.concatenate([B, np.full((1, 128), 255, np.uint8)])
+    row, col = oracle.top2(A, B2, L=L)
+    assert tuple(row[0]) == (0, -1, 0)                      # zero row: floor
+    assert row[1, 0] == 128 * 255 * 255 == 8323200         # all-255 pair
+    assert row[1, 1] == 5
+    assert row[1, 2] == 255 * int(B.astype(np.int64).sum(axis=1).max())
+    assert np.all(col[:, 1] == 1)                           # row 1 wins every column
+    assert np.all(col[:, 0] == 255 * B2.astype(np.int64).sum(axis=1))
+    # one-hot descriptors: the score is the product of the two hot values
+    Ah = np.zeros((2, 128), np.uint8)
+    Bh = np.zeros((3, 128), np.uint8)
+    Ah[0, 7], Ah[1, 9] = 200, 3
+    Bh[0, 7], Bh[1, 9], Bh[2, 7] = 11, 250, 13
+    row, col = oracle.top2(Ah, Bh, L=L)
+    assert row.tolist() == [[2600, 2, 2200], [750, 1, 0]]
+    assert col.tolist() == [[2200, 0], [750, 1], [2600, 0]]
+    assert oracle.match_pair(np.zeros((0, 128), np.uint8), B, L=L).shape == (0, 2)
+    assert oracle.match_pair(A, np.zeros((0, 128), np.uint8), L=L).shape == (0, 2)
+
+
+def pin_gate_closed_cases(L):
+    """Angles at the ends of the range and the ratio test's closed cases."""
+    assert oracle.angle(0, L=L) == math.acos(0.0)          # pi/2
+    assert abs(oracle.angle(0, L=L) - math.pi / 2) < 1e-15
+    assert oracle.angle(NORM2, L=L) == 0.0
+    assert oracle.angle(NORM2 + 12345, L=L) == 0.0          # clamped cosine
+    assert abs(oracle.angle(NORM2 // 2, L=L) - math.pi / 3) < 4e-16
+    s = np.arange(0, NORM2 + 1, 97)
+    d = np.array([oracle.angle(int(v), L=L) for v in s])
+    assert np.all(np.diff(d) < 0)                           # strictly decreasing
+    acc = lambda *a, **k: oracle.accept(*a, L=L, **k)
+    # s1 >= 512^2 > s2: d1 = 0 < r * d2
+    assert acc(0, NORM2, 3, NORM2 - 1, 0)
+    # both saturated: d1 = d2 = 0, 0 < 0 fails
+    assert not acc(0, NORM2, 3, NORM2 + 5, 0)
+    # a tie is rejected for r <= 1 and accepted for r > 1 (d1 > 0)
+    assert not acc(0, 200000, 3, 200000, 0, max_ratio=1.0)
+    assert acc(0, 200000, 3, 200000, 0, max_ratio=1.0001)
+    # one column: second = 0, d2 = pi/2; threshold at cos(0.4 pi) * 512^2
+    thr = math.cos(0.8 * math.pi / 2) * NORM2               # about 81,007
+    assert acc(0, int(thr) + 1, 0, 0, 0)
+    assert not acc(0, int(thr) - 1, 0, 0, 0)
+    # the distance gate is inclusive
+    d1 = oracle.angle(150000, L=L)
+    assert acc(0, 150000, 1, 0, 0, max_distance=d1)
+    assert not acc(0, 150000, 1, 0, 0, max_distance=np.nextafter(d1, 0))
+    # no candidate, and the cross-check
+    assert not acc(0, 0, -1, 0, -1)
+    assert not acc(4, 300000, 1, 0, 3)
+    assert acc(4, 300000, 1, 0, 3, cross_check=False)
+
+
+def _sparse(rows):
+    X = np.zeros((len(rows), 128), dtype=np.uint8)
+    for r, entries in enumerate(rows):
+        for dim, val in entries:
+            X[r, dim] = val
+    return X
+
+
+def golden_cases():
+    out = []
+    for fn in sorted(os.listdir(GOLDEN)):
+        if fn.endswith(".json"):
+            with open(os.path.join(GOLDEN, fn)) as f:
+                doc = json.load(f)
+            for case in doc["cases"]:
+                out.append((fn, case))
+    return out
+
+
+def pin_golden(L):
+    """Hand-derived fixtures (tests/golden/*.json)."""
+    cases = golden_cases()
+    assert cases
+    for fn, c in cases:
+        A, B = _sparse(c["A"]), _sparse(c["B"])
+        row, col = oracle.top2(A, B, L=L)
+        assert row.tolist() == c["row_top2"], (fn, c["name"], "row")
+        assert col.tolist() == c["col_best"], (fn, c["name"], "col")
+        p = c["params"]
+        md = math.inf if p["max_distance"] is None else p["max_distance"]
+        got = oracle.match_pair(A, B, p["max_ratio"], md, p["cross_check"], L=L)
+        assert got.tolist() == c["matches"], (fn, c["name"], "matches")
+
+
+def pin_planted(L):
+    """Planted correspondences are all recovered, nothing else is matched."""
+    for nA, nB, frac, k, md in ((1000, 1200, 0.30, 3, math.inf),
+                               (2048, 2048, 0.20, 4, 0.7)):
+        p = synth.pair(nA, nB, frac, k, 0)
+        got = oracle.match_pair(p.A, p.B, 0.8, md, True, L=L)
+        truth = {tuple(t) for t in p.truth.tolist()}
+        found = {tuple(t) for t in got.astype(np.int64).tolist()}
+        assert found == truth, (nA, nB, len(found & truth), len(truth),
+                                len(found - truth))
+
+
+def pin_invariants(L):
+    """Cross-checked output is mutual, one-to-one and sorted by row."""
+    p = synth.edge_pair(600, 700, 150, 30, False, 5)
+    row, col = oracle.top2(p.A, p.B, L=L)
+    got = oracle.match_pair(p.A, p.B, 0.8, math.inf, True, L=L).astype(np.int64)
+    assert len(got) > 50
+    assert np.all(np.diff(got[:, 0]) > 0)
+    assert len(set(got[:, 1].tolist())) == len(got)
+    for a, b in got.tolist():
+        assert row[a, 1] == b and col[b, 1] == a
+    # every duplicated best (a tie) is rejected at ratio 0.8
+    ties = np.flatnonzero((row[:, 0] == row[:, 2]) & (row[:, 1] >= 0))
+    assert len(ties) > 0 and not set(ties.tolist()) & set(got[:, 0].tolist())
+
+
+PINS = [pin_brute_tiny, pin_numpy_scores, pin_closed_forms,
+        pin_gate_closed_cases, pin_golden, pin_planted, pin_invariants]
