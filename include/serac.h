@@ -1,0 +1,145 @@
+/*
+ * serac.h - C ABI of the MI355X (gfx950) SIFT descriptor matcher.
+ *
+ * The library matches 128-dimensional unsigned 8-bit SIFT descriptors
+ * between image pairs by brute force, as the SERAC README describes (its
+ * introduction and the sections "What changed" and "Exactness"):
+ *
+ *   S[i][j] = sum_k A[i][k] * B[j][k]           exact integer inner product
+ *   row i   : (best, idx, second) over all j    identity (0, -1, 0), lowest
+ *                                                column on a tie, second
+ *                                                counted with multiplicity
+ *   col j   : (best, idx) over all i            lowest row on a tie
+ *   accept  : idx >= 0 and d1 <= max_distance and d1 < max_ratio * d2 and
+ *             (cross_check == 0 or col_idx[idx] == i),
+ *             where d = acos(min(s, 512^2) / 512^2) in IEEE double.
+ *
+ * The S matrix is never written to memory: the kernels reduce it to the
+ * row top-2 and the column best as they compute it.
+ *
+ * Conventions for every entry point:
+ *   - Descriptor arrays are device pointers to n rows of exactly 128 bytes,
+ *     row-major, 16-byte aligned.  The caller owns them; the library only
+ *     reads them.
+ *   - Output arrays are device pointers owned by the caller.
+ *   - Work is enqueued on the given HIP stream (NULL = the null stream) and
+ *     is asynchronous: results are valid once that stream has synchronised.
+ *     Temporary device memory is taken from the device's stream-ordered
+ *     pool on that stream and returned on it.
+ *   - Results are deterministic: they do not depend on occupancy, launch
+ *     order or the number of compute units.
+ *   - Arguments are validated before any HIP call; on an error nothing is
+ *     enqueued and no output is written.
+ *   - Only gfx950 devices are supported; any other device is refused with
+ *     SERAC_ERR_UNSUPPORTED_DEVICE (there is no fallback path).
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef SERAC_H
+#define SERAC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define SERAC_OK 0
+#define SERAC_ERR_INVALID_ARG (-1)        /* NULL with n > 0, n < 0, n too large, bad params */
+#define SERAC_ERR_CAPACITY (-2)           /* output capacity smaller than nA */
+#define SERAC_ERR_UNSUPPORTED_DEVICE (-3) /* current device is not gfx950 */
+#define SERAC_ERR_OUT_OF_MEMORY (-4)      /* device workspace allocation failed */
+#define SERAC_ERR_HIP (-5)                /* any other HIP runtime error */
+
+/* Largest descriptor count per image the library accepts. */
+#define SERAC_MAX_DESCRIPTORS 262144
+
+/* Matching parameters.
+ *   max_ratio    ratio test on angles, accept iff d1 < max_ratio * d2;
+ *                finite and > 0 (0.8 is the README's default; values above
+ *                1 are allowed and then a top-1 tie can pass).
+ *   max_distance accept iff d1 <= max_distance (radians); >= 0, +INFINITY
+ *                disables the gate; NaN is an error.
+ *   cross_check  0 or 1: require row i to be the best row of its best
+ *                column (lowest row on a tie).
+ *   flags        reserved, must be 0.
+ *   stream       hipStream_t to enqueue on; NULL selects the null stream. */
+typedef struct serac_params {
+    double max_ratio;
+    double max_distance;
+    int32_t cross_check;
+    int32_t flags;
+    void *stream;
+} serac_params;
+
+/* One correspondence: row a of the first set, row b of the second. */
+typedef struct serac_match {
+    uint32_t a;
+    uint32_t b;
+} serac_match;
+
+/* Output of one pair.  matches: device array of capacity entries, filled in
+ * ascending order of a; count: device int32 receiving the number written.
+ * capacity must be at least nA (each row yields at most one match). */
+typedef struct serac_matches {
+    serac_match *matches;
+    int64_t capacity;
+    int32_t *count;
+} serac_matches;
+
+/* A pair of image indices into a batch. */
+typedef struct serac_pair {
+    int32_t a;
+    int32_t b;
+} serac_pair;
+
+/*
+ * Match one pair: descA [nA][128] against descB [nB][128] (device).
+ * Implements the README's fused matcher (sections "What changed" and
+ * "Exactness"): the ratio test on the best and second-best score of each
+ * row, the optional max-distance gate and the optional mutual cross-check
+ * against the best of each column.
+ * nA or nB may be 0 (then *count is set to 0).  0 <= n <= SERAC_MAX_DESCRIPTORS.
+ * Errors: SERAC_ERR_INVALID_ARG, SERAC_ERR_CAPACITY, SERAC_ERR_UNSUPPORTED_DEVICE,
+ * SERAC_ERR_OUT_OF_MEMORY, SERAC_ERR_HIP.
+ */
+int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB,
+                     int32_t nB, const serac_params *params,
+                     const serac_matches *out_matches);
+
+/*
+ * Match many pairs of one image set in one call, as exhaustive matching
+ * over all image pairs does (README introduction: 589 images matched over
+ * all 173,166 pairs).
+ *   desc      host array [num_images] of device pointers to [n[k]][128]
+ *   n         host array [num_images] of descriptor counts
+ *   pairs     host array [num_pairs] of image index pairs (a, b)
+ *   out_matches host array [num_pairs]; out_matches[p] receives pair p's
+ *             matches (capacity >= n[pairs[p].a]).
+ * Every pair gets exactly the result serac_match_pair would give it.
+ * The host arrays may be released when the call returns.
+ */
+int serac_match_pairs(const uint8_t *const *desc, const int32_t *n,
+                      int32_t num_images, const serac_pair *pairs,
+                      int32_t num_pairs, const serac_params *params,
+                      const serac_matches *out_matches);
+
+/*
+ * The reductions behind the match list, exported for inspection:
+ *   row_top2 device int32 [nA][3] = (best, idx, second) per row of A
+ *   col_best device int32 [nB][2] = (best, idx) per row of B
+ * with the semantics in the header comment above.  Same ownership, stream
+ * and error rules as serac_match_pair; nA or nB may be 0.
+ */
+int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB,
+                    int32_t nB, void *stream, int32_t *row_top2,
+                    int32_t *col_best);
+
+/* Human-readable text for a status code (static storage). */
+const char *serac_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SERAC_H */

@@ -1,0 +1,177 @@
+"""MI355X (gfx950) fused SIFT descriptor matcher: thin Python binding.
+
+The C ABI in ``include/serac.h`` does all the work in HIP kernels; this
+module only marshals torch CUDA tensors (device memory and the current
+stream) into its arguments.  It never computes a step of the matcher
+itself and has no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["match_pair", "match_pair_into", "match_pairs", "top2",
+           "SeracError", "library", "LIB_PATH"]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libserac.so")
+MAX_DESCRIPTORS = 262144
+
+SERAC_OK = 0
+SERAC_ERR_INVALID_ARG = -1
+SERAC_ERR_CAPACITY = -2
+SERAC_ERR_UNSUPPORTED_DEVICE = -3
+SERAC_ERR_OUT_OF_MEMORY = -4
+SERAC_ERR_HIP = -5
+
+
+class serac_params(ctypes.Structure):
+    _fields_ = [("max_ratio", ctypes.c_double), ("max_distance", ctypes.c_double),
+                ("cross_check", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("stream", ctypes.c_void_p)]
+
+
+class serac_matches(ctypes.Structure):
+    _fields_ = [("matches", ctypes.c_void_p), ("capacity", ctypes.c_int64),
+                ("count", ctypes.c_void_p)]
+
+
+class serac_pair(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_int32), ("b", ctypes.c_int32)]
+
+
+class SeracError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {library().serac_status_string(status).decode()} "
+                         f"(status {status})")
+
+
+_lib = None
+
+
+def library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """The loaded C ABI.  Raises if the library has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library {path} is missing: build it with "
+                           "__graft_entry__.build() (hipcc, gfx950)")
+    L = ctypes.CDLL(path)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    L.serac_match_pair.argtypes = [vp, i32, vp, i32, ctypes.POINTER(serac_params),
+                                   ctypes.POINTER(serac_matches)]
+    L.serac_match_pairs.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(i32), i32,
+                                    ctypes.POINTER(serac_pair), i32,
+                                    ctypes.POINTER(serac_params),
+                                    ctypes.POINTER(serac_matches)]
+    L.serac_top2_pair.argtypes = [vp, i32, vp, i32, vp, vp, vp]
+    L.serac_status_string.argtypes = [ctypes.c_int]
+    L.serac_status_string.restype = ctypes.c_char_p
+    for f in (L.serac_match_pair, L.serac_match_pairs, L.serac_top2_pair):
+        f.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check_desc(x, name):
+    import torch
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.uint8 or x.dim() != 2 \
+            or x.shape[1] != 128 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous torch.uint8 CUDA tensor [n, 128]")
+    if x.shape[0] > MAX_DESCRIPTORS:
+        raise ValueError(f"{name} has more than {MAX_DESCRIPTORS} descriptors")
+
+
+def _params(max_ratio, max_distance, cross_check, stream):
+    return serac_params(float(max_ratio), float(max_distance), int(bool(cross_check)),
+                        0, ctypes.c_void_p(stream))
+
+
+def _stream(device):
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def match_pair_into(a, b, out, count, max_ratio=0.8, max_distance=math.inf,
+                    cross_check=True, stream=None) -> None:
+    """Enqueue one pair; out is int32 [>= nA, 2], count int32 [1] (device).
+
+    Asynchronous on the current stream (or ``stream``, a raw hipStream_t);
+    nothing is synchronised.
+    """
+    _check_desc(a, "a")
+    _check_desc(b, "b")
+    s = _stream(a.device) if stream is None else stream
+    p = _params(max_ratio, max_distance, cross_check, s)
+    m = serac_matches(out.data_ptr(), out.shape[0], count.data_ptr())
+    rc = library().serac_match_pair(a.data_ptr(), a.shape[0], b.data_ptr(), b.shape[0],
+                                    ctypes.byref(p), ctypes.byref(m))
+    if rc != SERAC_OK:
+        raise SeracError(rc, "serac_match_pair")
+
+
+def match_pair(a, b, max_ratio=0.8, max_distance=math.inf, cross_check=True):
+    """Matches of one pair as int32 [count, 2] = (row of a, row of b).
+
+    Synchronises the stream to read the count.
+    """
+    import torch
+    out = torch.empty((max(a.shape[0], 1), 2), dtype=torch.int32, device=a.device)
+    count = torch.empty(1, dtype=torch.int32, device=a.device)
+    match_pair_into(a, b, out, count, max_ratio, max_distance, cross_check)
+    return out[: int(count.item())]
+
+
+def match_pairs(images, pairs, max_ratio=0.8, max_distance=math.inf,
+                cross_check=True):
+    """Match many pairs of one image set in one call.
+
+    images: list of uint8 CUDA tensors [n_k, 128] on one device;
+    pairs: sequence of (a, b) image indices.  Returns a list of int32
+    [count, 2] tensors, one per pair, in order.
+    """
+    import torch
+    for k, x in enumerate(images):
+        _check_desc(x, f"images[{k}]")
+    pairs = [(int(p[0]), int(p[1])) for p in pairs]
+    P = len(pairs)
+    if P == 0:
+        return []
+    dev = images[0].device
+    caps = [max(images[a].shape[0], 1) for a, _ in pairs]
+    offs = [0]
+    for c in caps:
+        offs.append(offs[-1] + c)
+    out = torch.empty((offs[-1], 2), dtype=torch.int32, device=dev)
+    counts = torch.empty(P, dtype=torch.int32, device=dev)
+    ptrs = (ctypes.c_void_p * len(images))(*[x.data_ptr() for x in images])
+    ns = (ctypes.c_int32 * len(images))(*[x.shape[0] for x in images])
+    cp = (serac_pair * P)(*[serac_pair(a, b) for a, b in pairs])
+    ms = (serac_matches * P)(*[
+        serac_matches(out.data_ptr() + offs[k] * 8, caps[k], counts.data_ptr() + 4 * k)
+        for k in range(P)])
+    prm = _params(max_ratio, max_distance, cross_check, _stream(dev))
+    rc = library().serac_match_pairs(ptrs, ns, len(images), cp, P, ctypes.byref(prm), ms)
+    if rc != SERAC_OK:
+        raise SeracError(rc, "serac_match_pairs")
+    cnt = counts.cpu().tolist()
+    return [out[offs[k]: offs[k] + cnt[k]] for k in range(P)]
+
+
+def top2(a, b):
+    """(row_top2 int32 [nA, 3] = best, idx, second; col_best int32 [nB, 2])."""
+    import torch
+    _check_desc(a, "a")
+    _check_desc(b, "b")
+    row = torch.empty((a.shape[0], 3), dtype=torch.int32, device=a.device)
+    col = torch.empty((b.shape[0], 2), dtype=torch.int32, device=a.device)
+    rc = library().serac_top2_pair(a.data_ptr(), a.shape[0], b.data_ptr(), b.shape[0],
+                                   ctypes.c_void_p(_stream(a.device)),
+                                   row.data_ptr() if a.shape[0] else None,
+                                   col.data_ptr() if b.shape[0] else None)
+    if rc != SERAC_OK:
+        raise SeracError(rc, "serac_top2_pair")
+    return row, col

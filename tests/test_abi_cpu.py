@@ -1,0 +1,123 @@
+"""The C ABI on the CPU: it loads, exports what the header declares, and
+rejects bad arguments before touching HIP (no compute call is made)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import sift_descriptor_nearest_amd as serac
+from sift_descriptor_nearest_amd import serac_matches, serac_pair, serac_params
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "serac.h")
+FAKE = 0x10000          # never dereferenced: validation fails first
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(serac_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    L = serac.library()
+    names = declared()
+    assert {"serac_match_pair", "serac_match_pairs", "serac_top2_pair",
+            "serac_status_string"} <= set(names)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = serac.library()
+    for st in (0, -1, -2, -3, -4, -5):
+        assert L.serac_status_string(st)
+    assert L.serac_status_string(12345) == b"unknown status"
+
+
+def _p(**kw):
+    d = dict(max_ratio=0.8, max_distance=math.inf, cross_check=1, flags=0, stream=None)
+    d.update(kw)
+    return serac_params(d["max_ratio"], d["max_distance"], d["cross_check"], d["flags"],
+                        d["stream"])
+
+
+def _m(cap=100):
+    return serac_matches(FAKE, cap, FAKE)
+
+
+def call_pair(a=FAKE, nA=10, b=FAKE, nB=10, params="ok", out="ok"):
+    L = serac.library()
+    pp = ctypes.byref(_p()) if params == "ok" else params
+    oo = ctypes.byref(_m()) if out == "ok" else out
+    return L.serac_match_pair(a, nA, b, nB, pp, oo)
+
+
+BAD_PARAMS = [
+    dict(max_ratio=float("nan")), dict(max_ratio=0.0), dict(max_ratio=-1.0),
+    dict(max_ratio=math.inf), dict(max_distance=float("nan")),
+    dict(max_distance=-0.1), dict(cross_check=2), dict(cross_check=-1), dict(flags=1),
+]
+
+
+@pytest.mark.parametrize("kw", BAD_PARAMS, ids=[str(k) for k in BAD_PARAMS])
+def test_match_pair_rejects_bad_params(kw):
+    assert call_pair(params=ctypes.byref(_p(**kw))) == serac.SERAC_ERR_INVALID_ARG
+
+
+def test_match_pair_rejects_bad_sets():
+    E = serac.SERAC_ERR_INVALID_ARG
+    assert call_pair(a=None) == E
+    assert call_pair(b=None) == E
+    assert call_pair(nA=-1) == E
+    assert call_pair(nB=-5) == E
+    assert call_pair(nA=serac.MAX_DESCRIPTORS + 1) == E
+    assert call_pair(params=None) == E
+    assert call_pair(out=None) == E
+    assert call_pair(out=ctypes.byref(serac_matches(None, 100, FAKE))) == E
+    assert call_pair(out=ctypes.byref(serac_matches(FAKE, 100, None))) == E
+
+
+def test_match_pair_rejects_small_capacity():
+    assert call_pair(nA=101) == serac.SERAC_ERR_CAPACITY
+    assert call_pair(nA=10, out=ctypes.byref(_m(9))) == serac.SERAC_ERR_CAPACITY
+
+
+def test_match_pairs_validation():
+    L = serac.library()
+    ptrs = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    ns = (ctypes.c_int32 * 2)(10, 20)
+    ok = ctypes.byref(_p())
+
+    def run(pairs, outs, ns=ns, num_images=2, params=ok):
+        cp = (serac_pair * len(pairs))(*[serac_pair(*p) for p in pairs])
+        ms = (serac_matches * len(outs))(*outs)
+        return L.serac_match_pairs(ptrs, ns, num_images, cp, len(pairs), params, ms)
+
+    E = serac.SERAC_ERR_INVALID_ARG
+    assert run([(0, 2)], [_m()]) == E                     # image index out of range
+    assert run([(-1, 1)], [_m()]) == E
+    assert run([(0, 1)], [_m()], params=ctypes.byref(_p(flags=3))) == E
+    assert run([(1, 0)], [_m(19)]) == serac.SERAC_ERR_CAPACITY
+    assert run([(0, 1)], [serac_matches(FAKE, 100, None)]) == E
+    bad_n = (ctypes.c_int32 * 2)(10, -1)
+    assert run([(0, 1)], [_m()], ns=bad_n) == E
+    assert L.serac_match_pairs(ptrs, ns, -1, None, 0, ok, None) == E
+    # no pairs: nothing to do, nothing touched
+    assert L.serac_match_pairs(None, None, 0, None, 0, ok, None) == serac.SERAC_OK
+
+
+def test_top2_validation():
+    L = serac.library()
+    E = serac.SERAC_ERR_INVALID_ARG
+    assert L.serac_top2_pair(None, 3, FAKE, 3, None, FAKE, FAKE) == E
+    assert L.serac_top2_pair(FAKE, 3, FAKE, 3, None, None, FAKE) == E
+    assert L.serac_top2_pair(FAKE, 3, FAKE, 3, None, FAKE, None) == E
+    assert L.serac_top2_pair(FAKE, -3, FAKE, 3, None, FAKE, FAKE) == E
+
+
+def test_binding_rejects_non_tensors():
+    with pytest.raises(ValueError):
+        serac.match_pair_into(object(), object(), None, None)

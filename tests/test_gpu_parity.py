@@ -1,0 +1,188 @@
+"""The HIP path against the CPU oracle, through the C ABI.
+
+Match lists must be byte-identical (uint32 pairs, ascending row) and the
+top-2 export must equal the oracle's row top-2 and column best exactly:
+every score is an integer and the gates are one fixed double expression.
+Sizes span several 256-row blocks and 512-column chunks with ragged tails;
+the full-size workloads are checked in full where the oracle finishes in
+seconds (8192 x 8192) and on sampled rows and columns otherwise.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle_pins import tie_heavy
+from sift_descriptor_nearest_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def serac():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sift_descriptor_nearest_amd as s
+    s.library()
+    return s
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda:0")
+
+
+def check_pair(serac, A, B, max_ratio=0.8, max_distance=math.inf, cross_check=True,
+               top2=True, label=""):
+    say(f"[parity] {label} nA={len(A)} nB={len(B)} ratio={max_ratio} "
+        f"dist={max_distance} cross={cross_check}")
+    a, b = dev(A), dev(B)
+    got = serac.match_pair(a, b, max_ratio, max_distance, cross_check)
+    got = got.cpu().numpy().astype(np.uint32)
+    want = oracle.match_pair(A, B, max_ratio, max_distance, cross_check)
+    assert got.shape == want.shape, (label, got.shape, want.shape)
+    assert got.tobytes() == want.tobytes(), label
+    if top2:
+        row, col = serac.top2(a, b)
+        orow, ocol = oracle.top2(A, B)
+        assert np.array_equal(row.cpu().numpy(), orow), label + " row_top2"
+        assert np.array_equal(col.cpu().numpy(), ocol), label + " col_best"
+    return got
+
+
+SMALL = [(1, 1), (1, 2), (2, 1), (3, 17), (17, 3), (40, 40), (255, 511), (256, 512),
+         (257, 513), (300, 1100), (1029, 777), (513, 1537)]
+
+
+@pytest.mark.parametrize("nA,nB", SMALL, ids=[f"{a}x{b}" for a, b in SMALL])
+def test_tie_heavy_small(serac, nA, nB):
+    rng = np.random.default_rng(nA * 7919 + nB)
+    A = tie_heavy(rng, nA)
+    B = tie_heavy(rng, nB)
+    for r, cc in ((0.8, True), (1.5, True), (0.8, False)):
+        check_pair(serac, A, B, r, math.inf, cc, top2=(r == 0.8 and cc),
+                   label=f"tie-heavy {nA}x{nB}")
+
+
+@pytest.mark.parametrize("nA,nB", [(1000, 1200), (700, 2100), (2048, 96), (96, 2048),
+                                   (4099, 1031)])
+def test_planted_pairs(serac, nA, nB):
+    p = synth.pair(nA, nB, 0.3, 3, seed=nA + nB)
+    got = check_pair(serac, p.A, p.B, label=f"planted {nA}x{nB}")
+    assert len(got) > 0
+
+
+def test_workload_pair_1000x1200(serac):
+    p = synth.workload("pair_1000x1200")
+    got = check_pair(serac, p.A, p.B, **p.params(), label=p.name)
+    assert {tuple(x) for x in got.astype(np.int64).tolist()} == \
+        {tuple(x) for x in p.truth.tolist()}
+
+
+def test_workload_pair_8192x8192(serac):
+    p = synth.workload("pair_8192x8192")
+    check_pair(serac, p.A, p.B, **p.params(), label=p.name)
+
+
+@pytest.mark.parametrize("name", ["edge_8192x8192_ties", "edge_8192x8192_ties_no255",
+                                  "edge_8192x96_skinny", "edge_8192x96_skinny_no255"])
+def test_workload_edges(serac, name):
+    p = synth.workload(name)
+    check_pair(serac, p.A, p.B, **p.params(), label=name)
+    # the same pair through the other gates
+    check_pair(serac, p.A, p.B, 1.25, 0.7, True, top2=False, label=name + " r1.25 d0.7")
+    check_pair(serac, p.A, p.B, 0.8, math.inf, False, top2=False, label=name + " nocc")
+
+
+def test_empty_sides(serac):
+    rng = np.random.default_rng(5)
+    A = synth.desc(rng, 10)
+    E = np.zeros((0, 128), np.uint8)
+    for X, Y in ((A, E), (E, A), (E, E)):
+        a, b = dev(X), dev(Y)
+        assert serac.match_pair(a, b).shape[0] == 0
+        row, col = serac.top2(a, b)
+        assert row.cpu().tolist() == [[0, -1, 0]] * len(X)
+        assert col.cpu().tolist() == [[0, -1]] * len(Y)
+
+
+def test_zero_and_saturated_rows(serac):
+    A = np.zeros((300, 128), np.uint8)
+    B = np.zeros((600, 128), np.uint8)
+    A[17] = 255
+    A[200] = 255          # a duplicate: the column best must be row 17
+    B[599] = 255
+    B[3] = 1
+    check_pair(serac, A, B, label="zeros/255")
+
+
+def test_determinism_and_stream(serac):
+    p = synth.workload("edge_8192x8192_ties_no255")
+    a, b = dev(p.A), dev(p.B)
+    s = torch.cuda.Stream()
+    outs = []
+    for k in range(5):
+        out = torch.full((p.A.shape[0], 2), -1, dtype=torch.int32, device="cuda:0")
+        cnt = torch.full((1,), -7, dtype=torch.int32, device="cuda:0")
+        with torch.cuda.stream(s):
+            serac.match_pair_into(a, b, out, cnt)
+        s.synchronize()
+        outs.append(out[: int(cnt.item())].cpu().numpy().tobytes())
+    assert all(o == outs[0] for o in outs)
+    want = oracle.match_pair(p.A, p.B, 0.8, math.inf, True)
+    assert outs[0] == want.tobytes()
+
+
+def test_workload_pair_32768_sampled(serac):
+    p = synth.workload("pair_32768x32768")
+    a, b = dev(p.A), dev(p.B)
+    say("[parity] pair_32768x32768 GPU")
+    got = serac.match_pair(a, b, **p.params()).cpu().numpy().astype(np.int64)
+    row, col = serac.top2(a, b)
+    row, col = row.cpu().numpy(), col.cpu().numpy()
+    rng = np.random.default_rng(11)
+    sample = np.unique(np.concatenate([rng.choice(len(p.A), 192, replace=False),
+                                       p.truth[:64, 0], [0, len(p.A) - 1]])).astype(np.int32)
+    say(f"[parity] pair_32768x32768 oracle on {len(sample)} sampled rows")
+    dec = oracle.match_rows(p.A, p.B, sample, **p.params())
+    gmap = {int(x[0]): int(x[1]) for x in got}
+    for i in sample.tolist():
+        assert gmap.get(i, -1) == dec[i], i
+    assert np.array_equal(row[sample], oracle.rows(p.A, p.B, sample))
+    csample = np.unique(np.concatenate([rng.choice(len(p.B), 192, replace=False),
+                                        p.truth[:64, 1], [len(p.B) - 1]])).astype(np.int32)
+    assert np.array_equal(col[csample], oracle.cols(p.A, p.B, csample))
+    # properties at full size: sorted, one-to-one, mutual
+    assert np.all(np.diff(got[:, 0]) > 0)
+    assert len(np.unique(got[:, 1])) == len(got)
+    assert np.all(row[got[:, 0], 1] == got[:, 1]) and np.all(col[got[:, 1], 1] == got[:, 0])
+    assert {tuple(x) for x in p.truth.tolist()} <= {tuple(x) for x in got.tolist()}
+
+
+def test_batch_48x8192(serac):
+    bt = synth.exhaustive_48x8192()
+    imgs = [dev(x) for x in bt.images]
+    say(f"[parity] batch {len(bt.pairs)} pairs")
+    res = serac.match_pairs(imgs, bt.pairs.tolist(), **bt.params())
+    assert len(res) == len(bt.pairs)
+    # every pair equals the single-pair call on it
+    for k, (ia, ib) in enumerate(bt.pairs.tolist()):
+        one = serac.match_pair(imgs[ia], imgs[ib], **bt.params())
+        assert torch.equal(one, res[k]), (ia, ib)
+    # the oracle on a few pairs in full
+    for ia, ib in ((0, 1), (0, 2), (20, 47)):
+        k = int(np.flatnonzero((bt.pairs[:, 0] == ia) & (bt.pairs[:, 1] == ib))[0])
+        say(f"[parity] batch pair ({ia},{ib}) vs oracle")
+        want = oracle.match_pair(bt.images[ia], bt.images[ib], **bt.params())
+        assert res[k].cpu().numpy().astype(np.uint32).tobytes() == want.tobytes()
+        if (ia, ib) in bt.truth:
+            t = {tuple(x) for x in bt.truth[(ia, ib)].tolist()}
+            assert t <= {tuple(x) for x in want.astype(np.int64).tolist()}
