@@ -117,7 +117,9 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB,
  *   out_matches host array [num_pairs]; out_matches[p] receives pair p's
  *             matches (capacity >= n[pairs[p].a]).
  * Every pair gets exactly the result serac_match_pair would give it.
- * The host arrays may be released when the call returns.
+ * Unlike the other entry points this call returns only after the batch has
+ * completed on params->stream (it synchronises that stream), so the host
+ * arrays may be released as soon as it returns.
  */
 int serac_match_pairs(const uint8_t *const *desc, const int32_t *n,
                       int32_t num_images, const serac_pair *pairs,
@@ -134,6 +136,21 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n,
 int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB,
                     int32_t nB, void *stream, int32_t *row_top2,
                     int32_t *col_best);
+
+/*
+ * Profiling of the fused tile kernel (the kernel that does the contraction
+ * and the on-the-fly reductions).  serac_profile_start arms up to
+ * max_launches pairs of HIP events; every following launch of that kernel
+ * by serac_match_pair or serac_match_pairs records one event before and one
+ * after it on the call's stream.  serac_profile_stop waits for the recorded
+ * events, returns the summed device time in milliseconds and the number of
+ * launches timed, and disarms.  Not thread-safe against concurrent matching
+ * calls from other threads; meant for benchmarks.
+ * Errors: SERAC_ERR_INVALID_ARG (max_launches outside [1, 1048576], NULL
+ * outputs, stop without start), SERAC_ERR_HIP.
+ */
+int serac_profile_start(int32_t max_launches);
+int serac_profile_stop(double *tile_kernel_ms, int32_t *launches);
 
 /* Human-readable text for a status code (static storage). */
 const char *serac_status_string(int status);

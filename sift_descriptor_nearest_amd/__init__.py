@@ -12,7 +12,7 @@ import math
 import os
 
 __all__ = ["match_pair", "match_pair_into", "match_pairs", "top2",
-           "SeracError", "library", "LIB_PATH"]
+           "profile_start", "profile_stop", "SeracError", "library", "LIB_PATH"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libserac.so")
@@ -68,6 +68,10 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
                                     ctypes.POINTER(serac_params),
                                     ctypes.POINTER(serac_matches)]
     L.serac_top2_pair.argtypes = [vp, i32, vp, i32, vp, vp, vp]
+    L.serac_profile_start.argtypes = [i32]
+    L.serac_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
+    L.serac_profile_start.restype = ctypes.c_int
+    L.serac_profile_stop.restype = ctypes.c_int
     L.serac_status_string.argtypes = [ctypes.c_int]
     L.serac_status_string.restype = ctypes.c_char_p
     for f in (L.serac_match_pair, L.serac_match_pairs, L.serac_top2_pair):
@@ -175,3 +179,20 @@ def top2(a, b):
     if rc != SERAC_OK:
         raise SeracError(rc, "serac_top2_pair")
     return row, col
+
+
+def profile_start(max_launches: int) -> None:
+    """Arm HIP-event timing of the next max_launches tile-kernel launches."""
+    rc = library().serac_profile_start(int(max_launches))
+    if rc != SERAC_OK:
+        raise SeracError(rc, "serac_profile_start")
+
+
+def profile_stop():
+    """(summed tile-kernel device milliseconds, launches timed); disarms."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int32(0)
+    rc = library().serac_profile_stop(ctypes.byref(ms), ctypes.byref(n))
+    if rc != SERAC_OK:
+        raise SeracError(rc, "serac_profile_stop")
+    return ms.value, n.value

@@ -11,7 +11,7 @@
 // an ordered match list.
 //
 // How it maps to gfx950:
-//   * The contraction runs on v_mfma_i32_16x16x64_i8.  The MFMA is signed,
+//   * The contraction runs on v_mfma_i32_32x32x32_i8.  The MFMA is signed,
 //     so bytes enter as a' = a ^ 0x80 = a - 128 (exact) and the product is
 //     corrected with per-descriptor byte sums:
 //       S = sum a'b' + 128*SA_i + 128*SB_j - 2^21,
@@ -19,7 +19,7 @@
 //     The row term 128*SA_i - 2^21 enters through the MFMA accumulator input,
 //     so it costs no vector instruction.
 //   * A wave keeps the operand fragments of 64 rows of A in registers and
-//     sweeps 16-column tiles of B staged in LDS (512 columns per chunk).
+//     sweeps 32-column tiles of B staged in LDS (512 columns per chunk).
 //     Each score becomes one packed 32-bit key
 //       key = (S << 9) | (511 - local column),
 //     in one v_lshl_add (the column term 128*SB_j is folded into the addend),
@@ -46,6 +46,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -54,11 +55,13 @@
 namespace {
 
 constexpr int DIM = 128;
-constexpr int THREADS = 256;            // 4 waves of 64
-constexpr int ROWS_PER_WAVE = 64;
+constexpr int THREADS = 512;            // 8 waves of 64
+constexpr int ROWS_PER_WAVE = 32;       // one 32-row MFMA tile
 constexpr int ROWS_PER_BLOCK = 256;     // rows of A per workgroup pass
+constexpr int SLICE = 16;               // rows per column tie-break slice
 constexpr int CHUNK = 512;              // columns of B per LDS chunk (9-bit index)
-constexpr int TILES = CHUNK / 16;       // 16-column tiles per chunk
+constexpr int SUB = 128;                // columns per staged sub-chunk
+constexpr int NSUB = CHUNK / SUB;
 constexpr int MAX_CC_PER_WG = 4;        // chunks one workgroup sweeps
 constexpr int MAX_RB_PER_WG = 32;       // 32 blocks * 16 slices = 512 slice ids
 constexpr int NORM2 = 262144;           // 512^2
@@ -66,6 +69,7 @@ constexpr int FIN_THREADS = 256;
 constexpr int MAX_FIN = SERAC_MAX_DESCRIPTORS / FIN_THREADS;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 // One pair's work description and workspace.
 struct Job {
@@ -132,192 +136,241 @@ __device__ __forceinline__ int lds_off(int col, int part)
     return col * DIM + ((part ^ (col & 7)) << 4);
 }
 
-// Stage columns [cbase, cbase + 512) of B into LDS as int8 (a ^ 0x80), and
-// for each column the key addend P = ((128 * SB) << 9) + (511 - col).
-__device__ __forceinline__ void stage_chunk(const uint8_t *__restrict__ B, int nB,
-                                            int cbase, uint8_t *sB, uint32_t *sP,
+// A quarter of a chunk of B (SUB columns) in flight from global memory:
+// each thread holds 32 bytes (a quarter) of one column.
+struct SubRegs {
+    uint4 lo, hi;
+};
+
+__device__ __forceinline__ SubRegs load_sub(const uint8_t *__restrict__ B, int nB, int gcol0,
                                             int tid)
 {
-    constexpr int PARTS = CHUNK * DIM / 16 / THREADS;   // 16 per thread
-    uint4 v[PARTS];
-#pragma unroll
-    for (int q = 0; q < PARTS; ++q) {
-        const int e = q * THREADS + tid;
-        const int col = e >> 3, part = e & 7;
-        const int gcol = cbase + col;
-        v[q] = make_uint4(0u, 0u, 0u, 0u);
-        if (gcol < nB)
-            v[q] = *reinterpret_cast<const uint4 *>(B + (size_t)gcol * DIM + part * 16);
+    const int col = tid >> 2, q = tid & 3;
+    const int gcol = gcol0 + col;
+    SubRegs r;
+    r.lo = make_uint4(0u, 0u, 0u, 0u);
+    r.hi = r.lo;
+    if (gcol < nB) {
+        const uint8_t *p = B + (size_t)gcol * DIM + q * 32;
+        r.lo = *reinterpret_cast<const uint4 *>(p);
+        r.hi = *reinterpret_cast<const uint4 *>(p + 16);
     }
-#pragma unroll
-    for (int q = 0; q < PARTS; ++q) {
-        const int e = q * THREADS + tid;
-        const int col = e >> 3, part = e & 7;
-        uint32_t s = bytesum16(v[q]);
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-        if (part == 0)
-            sP[col] = ((s * 128u) << 9) + (uint32_t)(511 - col);
-        v4i x = to_i8(v[q]);
-        *reinterpret_cast<v4i *>(sB + lds_off(col, part)) = x;
-    }
+    return r;
 }
 
-// The fused tile sweep of one workgroup: row groups [rb0, rb1) of 256 rows
-// by column chunks [cc0, cc1) of 512 columns.
+// Write a quarter chunk into LDS as int8 (a ^ 0x80) at chunk columns
+// [col0, col0 + SUB), with each column's key addend
+//   P = ((128 * SB) << 9) + (511 - t),
+// t being the index of the column's 32-column tile among the tiles this
+// workgroup sweeps (t0 = index of the chunk's first tile).
+__device__ __forceinline__ void store_sub(const SubRegs &r, int col0, int t0, uint8_t *sB,
+                                          uint32_t *sP, int tid)
+{
+    const int col = col0 + (tid >> 2), q = tid & 3;
+    uint32_t s = bytesum16(r.lo) + bytesum16(r.hi);
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    if (q == 0)
+        sP[col] = ((s * 128u) << 9) + (uint32_t)(511 - (t0 + (col >> 5)));
+    *reinterpret_cast<v4i *>(sB + lds_off(col, 2 * q)) = to_i8(r.lo);
+    *reinterpret_cast<v4i *>(sB + lds_off(col, 2 * q + 1)) = to_i8(r.hi);
+}
+
+// The fused tile sweep of one workgroup: row blocks [rb0, rb1) of 256 rows
+// by column chunks [cc0, cc1) of 512 columns.  Each of the 8 waves owns 32
+// rows as one tile of v_mfma_i32_32x32x32_i8 (on gfx950 this MFMA leaves the
+// vector ALU free far more of the time than the 16x16x64 form does).  B is
+// double-buffered in LDS: while one chunk is swept, the next one (of this
+// row block, or the first of the next row block) is loaded a quarter at a
+// time into the other buffer.
+//
+// Accumulator layout of the 32x32 MFMA: lane l, register r holds output row
+// 8*(r/4) + 4*(l/32) + r%4 of column l%32.  The operand row that feeds
+// output row m is wave row 16*((m/4)%2) + 4*(m/8) + m%4, so lane half h,
+// register r is wave row 16*h + r: each lane half covers 16 consecutive
+// rows (one column tie-break slice).
+//
+// A lane only ever sees columns l%32 + 32*t of its workgroup's range, so
+// its running top-2 keys carry t (at most 64 tiles) in their low 9 bits and
+// stay valid across chunks; the 32 lanes sharing a row are merged once per
+// row block.
 template <bool COLS>
 __device__ __forceinline__ void tiles_body(const Job &J, int wgi)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t sB[CHUNK * DIM];   // 64 KiB
-    __shared__ uint32_t sP[CHUNK];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[2][CHUNK * DIM];   // 2 x 64 KiB
+    __shared__ uint32_t sP[2][CHUNK];
     __shared__ uint32_t sCol[COLS ? MAX_CC_PER_WG * CHUNK : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
-    const int n = lane & 15, g = lane >> 4;
+    const int n = lane & 31, h = lane >> 5;
     const int r = wgi % J.Gr, c = wgi / J.Gr;
     const int rb0 = r * J.rbPer, rb1 = min(rb0 + J.rbPer, J.nRB);
     const int cc0 = c * J.ccPer, cc1 = min(cc0 + J.ccPer, J.nCC);
     if (rb0 >= rb1 || cc0 >= cc1)
         return;
     const int nA = J.nA, nB = J.nB;
+    const int nchunks = cc1 - cc0;
 
     if (wgi == 0 && tid == 0)
         *J.ticket = 0u;   // the finishing kernel's arrival counter
     if (COLS) {
-        for (int k = tid; k < (cc1 - cc0) * CHUNK; k += THREADS)
+        for (int k = tid; k < nchunks * CHUNK; k += THREADS)
             sCol[k] = 0u;
     }
 
-    for (int rb = rb0; rb < rb1; ++rb) {
-        // ---- this wave's 64 rows of A: operand fragments and the row term
-        // The MFMA row m = 4*grp + reg of tile rt holds wave row
-        // 16*grp + 4*rt + reg, so lane group grp of the accumulator covers
-        // the 16 consecutive rows [16*grp, 16*grp + 16).
-        v4i af[4][2];
-        v4i ci[4];
+    // stage the first chunk
+    {
+        SubRegs q[NSUB];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            const int q = 16 * (n >> 2) + 4 * rt + (n & 3);
-            const int row = rb * ROWS_PER_BLOCK + w * ROWS_PER_WAVE + q;
-            uint4 x0 = make_uint4(0u, 0u, 0u, 0u), x1 = x0;
-            if (row < nA) {
-                const uint8_t *a = J.A + (size_t)row * DIM;
-                x0 = *reinterpret_cast<const uint4 *>(a + g * 16);
-                x1 = *reinterpret_cast<const uint4 *>(a + 64 + g * 16);
-            }
-            uint32_t s = bytesum16(x0) + bytesum16(x1);
-            s += __shfl_xor(s, 16);
-            s += __shfl_xor(s, 32);
-            af[rt][0] = to_i8(x0);
-            af[rt][1] = to_i8(x1);
+        for (int sq = 0; sq < NSUB; ++sq)
+            q[sq] = load_sub(J.B, nB, cc0 * CHUNK + sq * SUB, tid);
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                ci[rt][rr] = (int)(128u * (uint32_t)__shfl((int)s, 4 * g + rr)) - 2097152;
-        }
+        for (int sq = 0; sq < NSUB; ++sq)
+            store_sub(q[sq], sq * SUB, 0, sB[0], sP[0], tid);
+    }
+    int buf = 0;
 
-        // running (best, idx, second) of wave row `lane` over the chunks
-        uint32_t S1 = 0u, S2 = 0u;
-        int32_t I1 = -1;
-        const int slice = (rb - rb0) * 16 + w * 4 + g;
+    for (int rb = rb0; rb < rb1; ++rb) {
+        // ---- this wave's 32 rows of A: operand fragments and the row term
+        v4i af[4];
+        v16i ci;
+        {
+            const int m = n;
+            const int q = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
+            const int row = rb * ROWS_PER_BLOCK + w * ROWS_PER_WAVE + q;
+            uint4 x[4];
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc)
+                x[kc] = make_uint4(0u, 0u, 0u, 0u);
+            if (row < nA) {
+                const uint8_t *a = J.A + (size_t)row * DIM + 16 * h;
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc)
+                    x[kc] = *reinterpret_cast<const uint4 *>(a + 32 * kc);
+            }
+            uint32_t s = bytesum16(x[0]) + bytesum16(x[1]) + bytesum16(x[2]) + bytesum16(x[3]);
+            s += __shfl_xor(s, 32);
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc)
+                af[kc] = to_i8(x[kc]);
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int mo = 8 * (rr >> 2) + 4 * h + (rr & 3);
+                ci[rr] = (int)(128u * (uint32_t)__shfl((int)s, mo)) - 2097152;
+            }
+        }
+        __syncthreads();                     // the chunk in sB[buf] is complete
+
+        uint32_t b1[16], b2[16];
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            b1[x] = 0u;
+            b2[x] = 0u;
+        }
+        const int slice = (rb - rb0) * (ROWS_PER_BLOCK / SLICE) + w * 2 + h;
+        const uint32_t tag = (uint32_t)(511 - slice);
 
         for (int cc = cc0; cc < cc1; ++cc) {
-            __syncthreads();                 // sB / sP free
-            stage_chunk(J.B, nB, cc * CHUNK, sB, sP, tid);
-            __syncthreads();
-
-            uint32_t b1[16], b2[16];
-#pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                b1[x] = 0u;
-                b2[x] = 0u;
+            // the chunk that follows this one in the sweep, if any
+            int ncc = cc + 1, nrb = rb;
+            if (ncc == cc1) {
+                ncc = cc0;
+                nrb = rb + 1;
             }
+            const bool pre = nrb < rb1;
+            const uint8_t *curB = sB[buf];
+            const uint32_t *curP = sP[buf];
             uint32_t *colbase = sCol + (COLS ? (cc - cc0) * CHUNK : 0);
 
-            for (int u = 0; u < TILES; u += 2) {
-                const int col0 = u * 16 + n, col1 = col0 + 16;
-                const v4i bf00 = *reinterpret_cast<const v4i *>(sB + lds_off(col0, g));
-                const v4i bf01 = *reinterpret_cast<const v4i *>(sB + lds_off(col0, 4 + g));
-                const v4i bf10 = *reinterpret_cast<const v4i *>(sB + lds_off(col1, g));
-                const v4i bf11 = *reinterpret_cast<const v4i *>(sB + lds_off(col1, 4 + g));
-                const uint32_t P0 = sP[col0], P1 = sP[col1];
-                v4i acc0[4], acc1[4];
+#pragma unroll 1
+            for (int sq = 0; sq < NSUB; ++sq) {
+                SubRegs nq;
+                if (pre)
+                    nq = load_sub(J.B, nB, ncc * CHUNK + sq * SUB, tid);
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-                    acc0[rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[rt][0], bf00, ci[rt], 0, 0, 0);
+                for (int up = 0; up < SUB / 64; ++up) {
+                    const int col0 = sq * SUB + up * 64 + n, col1 = col0 + 32;
+                    const uint32_t P0 = curP[col0], P1 = curP[col1];
+                    v16i acc0 = ci, acc1 = ci;
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-                    acc1[rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[rt][0], bf10, ci[rt], 0, 0, 0);
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-                    acc0[rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[rt][1], bf01, acc0[rt], 0, 0, 0);
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-                    acc1[rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[rt][1], bf11, acc1[rt], 0, 0, 0);
+                    for (int kc = 0; kc < 4; ++kc) {
+                        const v4i bf0 = *reinterpret_cast<const v4i *>(curB + lds_off(col0, 2 * kc + h));
+                        const v4i bf1 = *reinterpret_cast<const v4i *>(curB + lds_off(col1, 2 * kc + h));
+                        acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[kc], bf0, acc0, 0, 0, 0);
+                        acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[kc], bf1, acc1, 0, 0, 0);
+                    }
 
-                uint32_t cm0 = 0u, cm1 = 0u;
+                    uint32_t cm0 = 0u, cm1 = 0u;
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        const int x = rt * 4 + rr;
-                        const uint32_t k0 = ((uint32_t)acc0[rt][rr] << 9) + P0;
-                        const uint32_t k1 = ((uint32_t)acc1[rt][rr] << 9) + P1;
-                        const uint32_t md = umed3(b1[x], k0, k1);
-                        b1[x] = umax3(b1[x], k0, k1);
-                        b2[x] = max(b2[x], md);
+                    for (int rr = 0; rr < 16; ++rr) {
+                        const uint32_t k0 = ((uint32_t)acc0[rr] << 9) + P0;
+                        const uint32_t k1 = ((uint32_t)acc1[rr] << 9) + P1;
+                        const uint32_t md = umed3(b1[rr], k0, k1);
+                        b1[rr] = umax3(b1[rr], k0, k1);
+                        b2[rr] = max(b2[rr], md);
                         if (COLS) {
                             cm0 = max(cm0, k0);
                             cm1 = max(cm1, k1);
                         }
                     }
+                    if (COLS) {
+                        atomicMax(colbase + col0, (cm0 & ~511u) | tag);
+                        atomicMax(colbase + col1, (cm1 & ~511u) | tag);
+                    }
                 }
-                if (COLS) {
-                    const uint32_t tag = (uint32_t)(511 - slice);
-                    atomicMax(colbase + col0, (cm0 & ~511u) | tag);
-                    atomicMax(colbase + col1, (cm1 & ~511u) | tag);
-                }
+                if (pre)
+                    store_sub(nq, sq * SUB, nrb == rb ? (ncc - cc0) * (CHUNK / 32) : 0,
+                              sB[buf ^ 1], sP[buf ^ 1], tid);
             }
-
-            // ---- merge the 16 lanes that share each row (via LDS)
-            __syncthreads();                 // everyone done with sB
-            uint2 *scr = reinterpret_cast<uint2 *>(sB) + w * (ROWS_PER_WAVE * 16);
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int q = 16 * g + 4 * rt + rr;
-                    scr[q * 16 + ((n + q) & 15)] = make_uint2(b1[rt * 4 + rr], b2[rt * 4 + rr]);
-                }
-            }
-            __syncthreads();
-            uint32_t K1 = 0u, K2 = 0u;
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const uint2 e = scr[lane * 16 + ((k + lane) & 15)];
-                const uint32_t lo = min(K1, e.x);
-                K1 = max(K1, e.x);
-                K2 = umax3(lo, K2, e.y);
-            }
-            const uint32_t s1 = K1 >> 9, s2 = K2 >> 9;
-            const uint32_t lo = min(S1, s1);
-            S2 = umax3(lo, S2, s2);
-            if (s1 > S1) {
-                S1 = s1;
-                I1 = cc * CHUNK + 511 - (int)(K1 & 511u);
-            }
+            __syncthreads();                 // next chunk complete, this one free
+            buf ^= 1;
         }
 
-        const int row = rb * ROWS_PER_BLOCK + w * ROWS_PER_WAVE + lane;
-        if (row < nA)
+        // ---- merge the 32 lanes that share each row (via LDS, in the free
+        // buffer): lane pair (q, q + 32) folds 16 of the 32 entries of row q
+        // each; key ties (same score, same tile) go to the lower lane, which
+        // is the lower column.
+        uint2 *scr = reinterpret_cast<uint2 *>(sB[buf ^ 1]) + w * (ROWS_PER_WAVE * 32);
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const int q = 16 * h + rr;
+            scr[q * 32 + ((n + q) & 31)] = make_uint2(b1[rr], b2[rr]);
+        }
+        __syncthreads();
+        uint32_t K1 = 0u, K2 = 0u;
+        int L1 = 64;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int src = (16 * h + k) & 31;              // source lane (column)
+            const uint2 e = scr[n * 32 + ((src + n) & 31)];
+            const uint32_t lo = min(K1, e.x);
+            if (e.x > K1 || (e.x == K1 && src < L1))
+                L1 = src;
+            K1 = max(K1, e.x);
+            K2 = umax3(lo, K2, e.y);
+        }
+        {
+            const uint32_t o1 = __shfl_xor(K1, 32), o2 = __shfl_xor(K2, 32);
+            const int oL = __shfl_xor(L1, 32);
+            const uint32_t lo = min(K1, o1);
+            if (o1 > K1 || (o1 == K1 && oL < L1))
+                L1 = oL;
+            K1 = max(K1, o1);
+            K2 = umax3(lo, K2, o2);
+        }
+        __syncthreads();                     // scratch free
+        const uint32_t S1 = K1 >> 9, S2 = K2 >> 9;
+        const int32_t I1 = S1 ? cc0 * CHUNK + 32 * (511 - (int)(K1 & 511u)) + L1 : -1;
+        const int row = rb * ROWS_PER_BLOCK + w * ROWS_PER_WAVE + n;
+        if (h == 0 && row < nA)
             J.rowpart[(size_t)c * nA + row] = make_int4((int)S1, I1, (int)S2, 0);
     }
 
     if (COLS) {
         __syncthreads();
         const int base = cc0 * CHUNK;
-        for (int k = tid; k < (cc1 - cc0) * CHUNK; k += THREADS) {
+        for (int k = tid; k < nchunks * CHUNK; k += THREADS) {
             const int col = base + k;
             if (col < nB)
                 J.colpart[(size_t)r * nB + col] = sCol[k];
@@ -326,13 +379,13 @@ __device__ __forceinline__ void tiles_body(const Job &J, int wgi)
 }
 
 template <bool COLS>
-__global__ __launch_bounds__(THREADS, 2) void serac_tiles_one(Job J)
+__global__ __launch_bounds__(THREADS, 1) void serac_tiles_one(Job J)
 {
     tiles_body<COLS>(J, blockIdx.x);
 }
 
 template <bool COLS>
-__global__ __launch_bounds__(THREADS, 2) void serac_tiles_many(const Job *__restrict__ jobs,
+__global__ __launch_bounds__(THREADS, 1) void serac_tiles_many(const Job *__restrict__ jobs,
                                                                int wgPerJob)
 {
     const Job J = jobs[blockIdx.x / wgPerJob];
@@ -361,37 +414,98 @@ __device__ int32_t dot_exact(const uint8_t *a, const uint8_t *b)
 
 // Merge the column-group partials of row i (ascending column groups, so a
 // strictly greater score is needed to move the index: lowest column wins).
+// Loads are issued sixteen at a time so their latencies overlap.
 __device__ __forceinline__ void merge_row(const Job &J, int i, uint32_t &S1, int32_t &I1,
                                           uint32_t &S2)
 {
     S1 = 0u;
     S2 = 0u;
     I1 = -1;
-    for (int c = 0; c < J.Gc; ++c) {
-        const int4 p = J.rowpart[(size_t)c * J.nA + i];
-        const uint32_t s1 = (uint32_t)p.x, s2 = (uint32_t)p.z;
-        const uint32_t lo = min(S1, s1);
-        S2 = umax3(lo, S2, s2);
-        if (s1 > S1) {
-            S1 = s1;
-            I1 = p.y;
+    for (int c0 = 0; c0 < J.Gc; c0 += 16) {
+        int4 p[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            p[k] = (c0 + k < J.Gc) ? J.rowpart[(size_t)(c0 + k) * J.nA + i]
+                                   : make_int4(0, -1, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const uint32_t s1 = (uint32_t)p[k].x, s2 = (uint32_t)p[k].z;
+            const uint32_t lo = min(S1, s1);
+            S2 = umax3(lo, S2, s2);
+            if (s1 > S1) {
+                S1 = s1;
+                I1 = p[k].y;
+            }
         }
     }
 }
 
-// Best score of column j and the first 16-row slice reaching it.
+// Best score of column j and the first 16-row slice reaching it (ascending
+// row groups, strictly greater: the lowest slice wins).
 __device__ __forceinline__ void merge_col(const Job &J, int j, uint32_t &C1, int32_t &slice)
 {
     C1 = 0u;
     slice = -1;
-    for (int r = 0; r < J.Gr; ++r) {
-        const uint32_t key = J.colpart[(size_t)r * J.nB + j];
-        const uint32_t s = key >> 9;
-        if (s > C1) {
-            C1 = s;
-            slice = r * J.rbPer * 16 + 511 - (int)(key & 511u);
+    for (int r0 = 0; r0 < J.Gr; r0 += 16) {
+        uint32_t key[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            key[k] = (r0 + k < J.Gr) ? J.colpart[(size_t)(r0 + k) * J.nB + j] : 0u;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const uint32_t s = key[k] >> 9;
+            if (s > C1) {
+                C1 = s;
+                slice = (r0 + k) * J.rbPer * (ROWS_PER_BLOCK / SLICE) + 511 - (int)(key[k] & 511u);
+            }
         }
     }
+}
+
+// Exclusive prefix sum of n <= 4 * FIN_THREADS counts into off[0..n], by the
+// whole workgroup.
+__device__ void block_exclusive_scan(const int32_t *counts, int n, int32_t *off)
+{
+    __shared__ int32_t sWaveSum[FIN_THREADS / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int32_t v[4];
+    int32_t run = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int idx = tid * 4 + k;
+        v[k] = (idx < n) ? __hip_atomic_load(counts + idx, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)
+                         : 0;
+        run += v[k];
+    }
+    // inclusive scan of the per-thread totals within the wave
+    int32_t inc = run;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t t = __shfl_up(inc, d);
+        if (lane >= d)
+            inc += t;
+    }
+    if (lane == 63)
+        sWaveSum[wv] = inc;
+    __syncthreads();
+    int32_t base = 0, total = 0;
+#pragma unroll
+    for (int k = 0; k < FIN_THREADS / 64; ++k) {
+        base += (k < wv) ? sWaveSum[k] : 0;
+        total += sWaveSum[k];
+    }
+    int32_t e = base + inc - run;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int idx = tid * 4 + k;
+        if (idx < n)
+            off[idx] = e;
+        e += v[k];
+    }
+    if (tid == 0)
+        off[n] = total;
+    __syncthreads();
 }
 
 // Gates, cross-check and ordered compaction of one group of 256 rows; the
@@ -421,12 +535,12 @@ __device__ __forceinline__ void finish_body(const Job &J, int wg, const Gate &G)
             uint32_t C1;
             int32_t slice;
             merge_col(J, I1, C1, slice);
-            if (C1 != S1 || slice != (i >> 4)) {
+            if (C1 != S1 || slice != i / SLICE) {
                 acc = false;
             } else {
                 // a lower row of the same slice reaching the same score wins
                 const uint8_t *b = J.B + (size_t)I1 * DIM;
-                for (int i2 = i & ~15; i2 < i; ++i2) {
+                for (int i2 = i - i % SLICE; i2 < i; ++i2) {
                     if (sS1[i2 - wg * FIN_THREADS] >= C1 &&
                         (uint32_t)dot_exact(J.A + (size_t)i2 * DIM, b) == C1) {
                         acc = false;
@@ -465,15 +579,7 @@ __device__ __forceinline__ void finish_body(const Job &J, int wg, const Gate &G)
     if (!sLast)
         return;
     __threadfence();
-    if (tid == 0) {
-        int run = 0;
-        for (int k = 0; k < J.nFin; ++k) {
-            sOff[k] = run;
-            run += __hip_atomic_load(J.wgcount + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        sOff[J.nFin] = run;
-    }
-    __syncthreads();
+    block_exclusive_scan(J.wgcount, J.nFin, sOff);
     const int all = sOff[J.nFin];
     for (int p = tid; p < all; p += FIN_THREADS) {
         // group holding output position p: last k with sOff[k] <= p
@@ -550,7 +656,7 @@ __global__ void serac_export_cols(Job J, const uint32_t *s1, int32_t *col_best)
     int32_t idx = -1;
     if (C1 > 0u) {
         const uint8_t *b = J.B + (size_t)j * DIM;
-        for (int i = slice * 16; i < min(slice * 16 + 16, J.nA); ++i) {
+        for (int i = slice * SLICE; i < min(slice * SLICE + SLICE, J.nA); ++i) {
             if (s1[i] >= C1 && (uint32_t)dot_exact(J.A + (size_t)i * DIM, b) == C1) {
                 idx = i;
                 break;
@@ -572,6 +678,33 @@ struct Device {
 
 std::mutex g_mutex;
 Device g_devices[64];
+
+// Event pairs around tile-kernel launches while profiling is armed.
+struct Profile {
+    bool armed = false;
+    int used = 0;
+    std::vector<hipEvent_t> ev;   // [2 * max]: begin, end
+};
+std::mutex g_prof_mutex;
+Profile g_prof;
+
+int prof_begin(hipStream_t s)
+{
+    std::lock_guard<std::mutex> lock(g_prof_mutex);
+    if (!g_prof.armed || 2 * (g_prof.used + 1) > (int)g_prof.ev.size())
+        return -1;
+    const int slot = g_prof.used++;
+    (void)hipEventRecord(g_prof.ev[2 * slot], s);
+    return slot;
+}
+
+void prof_end(hipStream_t s, int slot)
+{
+    if (slot < 0)
+        return;
+    std::lock_guard<std::mutex> lock(g_prof_mutex);
+    (void)hipEventRecord(g_prof.ev[2 * slot + 1], s);
+}
 
 int hip_fail()
 {
@@ -625,6 +758,52 @@ int device_setup(Device **out)
     }
     *out = &d;
     return d.status;
+}
+
+// Grow-only workspace per (device, stream).  Work on one stream runs in
+// order, so consecutive calls on a stream can share one workspace; calls on
+// different streams get different ones.  Growth frees the old buffer and
+// allocates the new one on the same stream, both stream-ordered.
+struct Workspace {
+    int dev;
+    hipStream_t stream;
+    uint8_t *ptr;
+    size_t bytes;
+};
+std::mutex g_ws_mutex;
+std::vector<Workspace> g_ws;
+
+int get_workspace(hipStream_t stream, size_t bytes, uint8_t **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return hip_fail();
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace *w = nullptr;
+    for (auto &e : g_ws)
+        if (e.dev == dev && e.stream == stream)
+            w = &e;
+    if (w && w->bytes >= bytes) {
+        *out = w->ptr;
+        return SERAC_OK;
+    }
+    if (!w) {
+        g_ws.push_back(Workspace{dev, stream, nullptr, 0});
+        w = &g_ws.back();
+    }
+    if (w->ptr)
+        (void)hipFreeAsync(w->ptr, stream);
+    w->ptr = nullptr;
+    w->bytes = 0;
+    const size_t want = std::max(bytes, (size_t)1 << 20);
+    if (hipMallocAsync(reinterpret_cast<void **>(&w->ptr), want, stream) != hipSuccess) {
+        (void)hipGetLastError();
+        w->ptr = nullptr;
+        return SERAC_ERR_OUT_OF_MEMORY;
+    }
+    w->bytes = want;
+    *out = w->ptr;
+    return SERAC_OK;
 }
 
 struct Plan {
@@ -768,23 +947,22 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int
         serac_zero_counts<<<1, 64, 0, stream>>>(nullptr, out->count, 1);
         return hipGetLastError() == hipSuccess ? SERAC_OK : SERAC_ERR_HIP;
     }
-    const Plan p = make_plan(nA, nB, 2 * d->cus);
+    const Plan p = make_plan(nA, nB, d->cus);
     uint8_t *ws = nullptr;
-    if (hipMallocAsync(reinterpret_cast<void **>(&ws), plan_bytes(p), stream) != hipSuccess) {
-        (void)hipGetLastError();
-        return SERAC_ERR_OUT_OF_MEMORY;
-    }
+    st = get_workspace(stream, plan_bytes(p), &ws);
+    if (st != SERAC_OK)
+        return st;
     Job J;
     fill_job(J, p, descA, nA, descB, nB, ws, out->matches, out->count);
     const Gate G = make_gate(d, params);
+    const int slot = prof_begin(stream);
     if (params->cross_check)
         serac_tiles_one<true><<<p.Gr * p.Gc, THREADS, 0, stream>>>(J);
     else
         serac_tiles_one<false><<<p.Gr * p.Gc, THREADS, 0, stream>>>(J);
+    prof_end(stream, slot);
     serac_finish_one<<<p.nFin, FIN_THREADS, 0, stream>>>(J, G);
-    const hipError_t e = hipGetLastError();
-    (void)hipFreeAsync(ws, stream);
-    return e == hipSuccess ? SERAC_OK : SERAC_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? SERAC_OK : SERAC_ERR_HIP;
 }
 
 int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_images,
@@ -826,7 +1004,7 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
     }
     // workgroups per pair: enough to fill the device a few times over
     const int nlive = (int)live.size();
-    const int target = nlive ? std::max(1, (8 * d->cus + nlive - 1) / nlive) : 1;
+    const int target = nlive ? std::max(1, (4 * d->cus + nlive - 1) / nlive) : 1;
     std::vector<Plan> plans(nlive);
     size_t bytes = align256(sizeof(Job) * (size_t)std::max(nlive, 1)) +
                    align256(sizeof(int32_t *) * zero.size() + 8);
@@ -839,10 +1017,9 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
         finPerJob = std::max(finPerJob, plans[k].nFin);
     }
     uint8_t *ws = nullptr;
-    if (hipMallocAsync(reinterpret_cast<void **>(&ws), bytes, stream) != hipSuccess) {
-        (void)hipGetLastError();
-        return SERAC_ERR_OUT_OF_MEMORY;
-    }
+    st = get_workspace(stream, bytes, &ws);
+    if (st != SERAC_OK)
+        return st;
     std::vector<uint8_t> host(align256(sizeof(Job) * (size_t)std::max(nlive, 1)) +
                               align256(sizeof(int32_t *) * zero.size() + 8));
     Job *jobs = reinterpret_cast<Job *>(host.data());
@@ -866,15 +1043,16 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
                                                                          (int)zero.size());
     if (e == hipSuccess && nlive) {
         const Gate G = make_gate(d, params);
+        const int slot = prof_begin(stream);
         if (params->cross_check)
             serac_tiles_many<true><<<nlive * wgPerJob, THREADS, 0, stream>>>(djobs, wgPerJob);
         else
             serac_tiles_many<false><<<nlive * wgPerJob, THREADS, 0, stream>>>(djobs, wgPerJob);
+        prof_end(stream, slot);
         serac_finish_many<<<nlive * finPerJob, FIN_THREADS, 0, stream>>>(djobs, finPerJob, G);
     }
     if (e == hipSuccess)
         e = hipGetLastError();
-    (void)hipFreeAsync(ws, stream);
     if (e == hipSuccess) {
         // the staging buffer `host` must outlive the copy
         e = hipStreamSynchronize(stream);
@@ -895,13 +1073,12 @@ int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int3
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     if (nA == 0 && nB == 0)
         return SERAC_OK;
-    const Plan p = make_plan(std::max(nA, 1), std::max(nB, 1), 2 * d->cus);
+    const Plan p = make_plan(std::max(nA, 1), std::max(nB, 1), d->cus);
     size_t bytes = plan_bytes(p) + align256((size_t)std::max(nA, 1) * sizeof(uint32_t));
     uint8_t *ws = nullptr;
-    if (hipMallocAsync(reinterpret_cast<void **>(&ws), bytes, stream) != hipSuccess) {
-        (void)hipGetLastError();
-        return SERAC_ERR_OUT_OF_MEMORY;
-    }
+    st = get_workspace(stream, bytes, &ws);
+    if (st != SERAC_OK)
+        return st;
     Job J;
     fill_job(J, p, descA, nA, descB, nB, ws, nullptr, nullptr);
     uint32_t *s1 = reinterpret_cast<uint32_t *>(ws + plan_bytes(p));
@@ -918,9 +1095,57 @@ int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int3
         serac_export_rows<<<(nA + 255) / 256, 256, 0, stream>>>(E, row_top2, s1);
     if (nB > 0)
         serac_export_cols<<<(nB + 255) / 256, 256, 0, stream>>>(E, s1, col_best);
-    const hipError_t e = hipGetLastError();
-    (void)hipFreeAsync(ws, stream);
-    return e == hipSuccess ? SERAC_OK : SERAC_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? SERAC_OK : SERAC_ERR_HIP;
+}
+
+int serac_profile_start(int32_t max_launches)
+{
+    if (max_launches < 1 || max_launches > (1 << 20))
+        return SERAC_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lock(g_prof_mutex);
+    for (hipEvent_t e : g_prof.ev)
+        (void)hipEventDestroy(e);
+    g_prof.ev.clear();
+    g_prof.used = 0;
+    g_prof.armed = false;
+    g_prof.ev.resize(2 * (size_t)max_launches);
+    for (auto &e : g_prof.ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            e = nullptr;
+            return hip_fail();
+        }
+    }
+    g_prof.armed = true;
+    return SERAC_OK;
+}
+
+int serac_profile_stop(double *tile_kernel_ms, int32_t *launches)
+{
+    if (!tile_kernel_ms || !launches)
+        return SERAC_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lock(g_prof_mutex);
+    if (!g_prof.armed)
+        return SERAC_ERR_INVALID_ARG;
+    double total = 0.0;
+    int st = SERAC_OK;
+    for (int k = 0; k < g_prof.used; ++k) {
+        float ms = 0.f;
+        if (hipEventSynchronize(g_prof.ev[2 * k + 1]) != hipSuccess ||
+            hipEventElapsedTime(&ms, g_prof.ev[2 * k], g_prof.ev[2 * k + 1]) != hipSuccess) {
+            st = hip_fail();
+            break;
+        }
+        total += ms;
+    }
+    *tile_kernel_ms = total;
+    *launches = g_prof.used;
+    for (hipEvent_t e : g_prof.ev)
+        if (e)
+            (void)hipEventDestroy(e);
+    g_prof.ev.clear();
+    g_prof.used = 0;
+    g_prof.armed = false;
+    return st;
 }
 
 }  // extern "C"
