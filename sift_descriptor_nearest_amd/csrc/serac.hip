@@ -65,13 +65,15 @@ constexpr int NSUB = CHUNK / SUB;
 constexpr int MAX_CC_PER_WG = 4;        // chunks one workgroup sweeps
 constexpr int MAX_RB_PER_WG = 32;       // 32 blocks * 16 slices = 512 slice ids
 constexpr int NORM2 = 262144;           // 512^2
-constexpr int FIN_THREADS = 256;
-constexpr int MAX_FIN = SERAC_MAX_DESCRIPTORS / FIN_THREADS;
+constexpr int GATE_THREADS = 256;
+constexpr int COMPACT_THREADS = 1024;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-// One pair's work description and workspace.
+// One pair's work description and its accumulators.  The accumulators
+// are zero between calls: the tile kernel raises them with atomic maxima and
+// the finishing kernel reads them and clears them again.
 struct Job {
     const uint8_t *A;
     const uint8_t *B;
@@ -79,13 +81,10 @@ struct Job {
     int32_t nRB, nCC;        // row blocks of 256, column chunks of 512
     int32_t rbPer, ccPer;    // per workgroup
     int32_t Gr, Gc;          // workgroup grid (row groups x column groups)
-    int32_t nFin;            // finishing workgroups (256 rows each)
-    int32_t pad;
-    int4 *rowpart;           // [Gc][nA]   (best, idx, second, 0) per column group
-    uint32_t *colpart;       // [Gr][nB]   (best << 9) | (511 - slice)
-    uint2 *staging;          // [nFin][256] accepted (a, b) per finishing group
-    int32_t *wgcount;        // [nFin]
-    uint32_t *ticket;        // 1
+    unsigned long long *rbest;  // [nA] (best << 32) | ~column   (max: lowest column)
+    uint32_t *rsec;             // [nA] second-best score
+    unsigned long long *cbest;  // [nB] (best << 32) | ~slice    (max: lowest slice)
+    int32_t *res;            // [nA] accepted column of each row, or -1 (scratch)
     serac_match *out;        // [>= nA]
     int32_t *count;          // 1
 };
@@ -212,8 +211,6 @@ __device__ __forceinline__ void tiles_body(const Job &J, int wgi)
     const int nA = J.nA, nB = J.nB;
     const int nchunks = cc1 - cc0;
 
-    if (wgi == 0 && tid == 0)
-        *J.ticket = 0u;   // the finishing kernel's arrival counter
     if (COLS) {
         for (int k = tid; k < nchunks * CHUNK; k += THREADS)
             sCol[k] = 0u;
@@ -360,11 +357,20 @@ __device__ __forceinline__ void tiles_body(const Job &J, int wgi)
             K2 = umax3(lo, K2, o2);
         }
         __syncthreads();                     // scratch free
+        // publish this row block's top-2 over the workgroup's columns: the
+        // atomic max keeps the best key over all workgroups; whichever key
+        // loses an exchange (or this group's own second) raises the row's
+        // second score, so the second ends as the runner-up of all
+        // candidates, ties counted.
         const uint32_t S1 = K1 >> 9, S2 = K2 >> 9;
-        const int32_t I1 = S1 ? cc0 * CHUNK + 32 * (511 - (int)(K1 & 511u)) + L1 : -1;
         const int row = rb * ROWS_PER_BLOCK + w * ROWS_PER_WAVE + n;
-        if (h == 0 && row < nA)
-            J.rowpart[(size_t)c * nA + row] = make_int4((int)S1, I1, (int)S2, 0);
+        if (h == 0 && row < nA && S1 > 0u) {
+            const uint32_t col = (uint32_t)(cc0 * CHUNK + 32 * (511 - (int)(K1 & 511u)) + L1);
+            const unsigned long long key = ((unsigned long long)S1 << 32) | (0xFFFFFFFFu - col);
+            const unsigned long long old = atomicMax(J.rbest + row, key);
+            const uint32_t loser = (uint32_t)(min(old, key) >> 32);
+            atomicMax(J.rsec + row, max(loser, S2));
+        }
     }
 
     if (COLS) {
@@ -372,8 +378,13 @@ __device__ __forceinline__ void tiles_body(const Job &J, int wgi)
         const int base = cc0 * CHUNK;
         for (int k = tid; k < nchunks * CHUNK; k += THREADS) {
             const int col = base + k;
-            if (col < nB)
-                J.colpart[(size_t)r * nB + col] = sCol[k];
+            const uint32_t key = sCol[k];
+            if (col < nB && (key >> 9) > 0u) {
+                const uint32_t slice = (uint32_t)(r * J.rbPer * (ROWS_PER_BLOCK / SLICE) + 511 -
+                                                  (int)(key & 511u));
+                atomicMax(J.cbest + col,
+                          ((unsigned long long)(key >> 9) << 32) | (0xFFFFFFFFu - slice));
+            }
         }
     }
 }
@@ -412,208 +423,148 @@ __device__ int32_t dot_exact(const uint8_t *a, const uint8_t *b)
     return (int32_t)s;
 }
 
-// Merge the column-group partials of row i (ascending column groups, so a
-// strictly greater score is needed to move the index: lowest column wins).
-// Loads are issued sixteen at a time so their latencies overlap.
-__device__ __forceinline__ void merge_row(const Job &J, int i, uint32_t &S1, int32_t &I1,
-                                          uint32_t &S2)
+// Row i's published result: best score, its column (-1 below the zero
+// floor) and the second score.
+__device__ __forceinline__ void row_result(const Job &J, unsigned long long key, uint32_t sec,
+                                           uint32_t &S1, int32_t &I1, uint32_t &S2)
 {
-    S1 = 0u;
-    S2 = 0u;
-    I1 = -1;
-    for (int c0 = 0; c0 < J.Gc; c0 += 16) {
-        int4 p[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k)
-            p[k] = (c0 + k < J.Gc) ? J.rowpart[(size_t)(c0 + k) * J.nA + i]
-                                   : make_int4(0, -1, 0, 0);
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const uint32_t s1 = (uint32_t)p[k].x, s2 = (uint32_t)p[k].z;
-            const uint32_t lo = min(S1, s1);
-            S2 = umax3(lo, S2, s2);
-            if (s1 > S1) {
-                S1 = s1;
-                I1 = p[k].y;
-            }
-        }
-    }
+    S1 = (uint32_t)(key >> 32);
+    I1 = S1 ? (int32_t)(0xFFFFFFFFu - (uint32_t)key) : -1;
+    S2 = sec;
 }
 
-// Best score of column j and the first 16-row slice reaching it (ascending
-// row groups, strictly greater: the lowest slice wins).
-__device__ __forceinline__ void merge_col(const Job &J, int j, uint32_t &C1, int32_t &slice)
+// Gates and cross-check of 256 rows: res[i] = the accepted column of row i,
+// or -1.  The row accumulators are cleared as they are consumed.
+__device__ __forceinline__ void gate_body(const Job &J, int wg, const Gate &G)
 {
-    C1 = 0u;
-    slice = -1;
-    for (int r0 = 0; r0 < J.Gr; r0 += 16) {
-        uint32_t key[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k)
-            key[k] = (r0 + k < J.Gr) ? J.colpart[(size_t)(r0 + k) * J.nB + j] : 0u;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const uint32_t s = key[k] >> 9;
-            if (s > C1) {
-                C1 = s;
-                slice = (r0 + k) * J.rbPer * (ROWS_PER_BLOCK / SLICE) + 511 - (int)(key[k] & 511u);
-            }
-        }
-    }
-}
-
-// Exclusive prefix sum of n <= 4 * FIN_THREADS counts into off[0..n], by the
-// whole workgroup.
-__device__ void block_exclusive_scan(const int32_t *counts, int n, int32_t *off)
-{
-    __shared__ int32_t sWaveSum[FIN_THREADS / 64];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    int32_t v[4];
-    int32_t run = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int idx = tid * 4 + k;
-        v[k] = (idx < n) ? __hip_atomic_load(counts + idx, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT)
-                         : 0;
-        run += v[k];
-    }
-    // inclusive scan of the per-thread totals within the wave
-    int32_t inc = run;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int32_t t = __shfl_up(inc, d);
-        if (lane >= d)
-            inc += t;
-    }
-    if (lane == 63)
-        sWaveSum[wv] = inc;
-    __syncthreads();
-    int32_t base = 0, total = 0;
-#pragma unroll
-    for (int k = 0; k < FIN_THREADS / 64; ++k) {
-        base += (k < wv) ? sWaveSum[k] : 0;
-        total += sWaveSum[k];
-    }
-    int32_t e = base + inc - run;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int idx = tid * 4 + k;
-        if (idx < n)
-            off[idx] = e;
-        e += v[k];
-    }
-    if (tid == 0)
-        off[n] = total;
-    __syncthreads();
-}
-
-// Gates, cross-check and ordered compaction of one group of 256 rows; the
-// last group to arrive concatenates all groups' matches in row order.
-__device__ __forceinline__ void finish_body(const Job &J, int wg, const Gate &G)
-{
-    __shared__ uint32_t sS1[FIN_THREADS];
-    __shared__ int32_t sWave[FIN_THREADS / 64];
-    __shared__ int32_t sOff[MAX_FIN + 1];
-    __shared__ int32_t sLast;
-
+    __shared__ uint32_t sS1[GATE_THREADS];
     const int tid = threadIdx.x;
-    const int i = wg * FIN_THREADS + tid;
+    const int i = wg * GATE_THREADS + tid;
     uint32_t S1 = 0u, S2 = 0u;
     int32_t I1 = -1;
-    if (i < J.nA)
-        merge_row(J, i, S1, I1, S2);
+    if (i < J.nA) {
+        row_result(J, J.rbest[i], J.rsec[i], S1, I1, S2);
+        J.rbest[i] = 0ull;
+        J.rsec[i] = 0u;
+    }
     sS1[tid] = S1;
-    __syncthreads();
-
-    bool acc = false;
-    if (i < J.nA && I1 >= 0 && I1 < J.nB) {
-        const double d1 = G.table[min(S1, (uint32_t)NORM2)];
-        const double d2 = G.table[min(S2, (uint32_t)NORM2)];
-        acc = (d1 <= G.max_distance) && (d1 < G.max_ratio * d2);
-        if (acc && G.cross_check) {
-            uint32_t C1;
-            int32_t slice;
-            merge_col(J, I1, C1, slice);
-            if (C1 != S1 || slice != i / SLICE) {
-                acc = false;
-            } else {
-                // a lower row of the same slice reaching the same score wins
-                const uint8_t *b = J.B + (size_t)I1 * DIM;
-                for (int i2 = i - i % SLICE; i2 < i; ++i2) {
-                    if (sS1[i2 - wg * FIN_THREADS] >= C1 &&
-                        (uint32_t)dot_exact(J.A + (size_t)i2 * DIM, b) == C1) {
-                        acc = false;
-                        break;
-                    }
+    const bool cand = I1 >= 0 && I1 < J.nB;
+    double d1 = 0.0, d2 = 0.0;
+    unsigned long long cb = 0ull;
+    if (cand) {
+        d1 = G.table[min(S1, (uint32_t)NORM2)];
+        d2 = G.table[min(S2, (uint32_t)NORM2)];
+        if (G.cross_check)
+            cb = J.cbest[I1];
+    }
+    __syncthreads();                         // sS1 complete
+    if (i >= J.nA)
+        return;
+    bool acc = cand && (d1 <= G.max_distance) && (d1 < G.max_ratio * d2);
+    if (acc && G.cross_check) {
+        const uint32_t C1 = (uint32_t)(cb >> 32);
+        const int32_t slice = (int32_t)(0xFFFFFFFFu - (uint32_t)cb);
+        if (C1 != S1 || slice != i / SLICE) {
+            acc = false;
+        } else {
+            // a lower row of the same slice reaching the same score wins
+            const uint8_t *b = J.B + (size_t)I1 * DIM;
+            for (int i2 = i - i % SLICE; i2 < i; ++i2) {
+                if (sS1[i2 - wg * GATE_THREADS] >= C1 &&
+                    (uint32_t)dot_exact(J.A + (size_t)i2 * DIM, b) == C1) {
+                    acc = false;
+                    break;
                 }
             }
         }
     }
+    J.res[i] = acc ? I1 : -1;
+}
 
-    // ordered compaction within the group
-    const int lane = tid & 63, wv = tid >> 6;
-    const uint64_t mask = __ballot(acc);
-    const int before = __popcll(mask & ((1ull << lane) - 1ull));
-    if (lane == 0)
-        sWave[wv] = __popcll(mask);
-    __syncthreads();
-    int base = 0, total = 0;
-    for (int k = 0; k < FIN_THREADS / 64; ++k) {
-        base += (k < wv) ? sWave[k] : 0;
-        total += sWave[k];
-    }
-    if (acc)
-        J.staging[(size_t)wg * FIN_THREADS + base + before] = make_uint2((uint32_t)i, (uint32_t)I1);
-    if (tid == 0)
-        J.wgcount[wg] = total;
+__global__ __launch_bounds__(GATE_THREADS) void serac_gate_one(Job J, Gate G)
+{
+    gate_body(J, blockIdx.x, G);
+}
 
-    // arrival; the last group concatenates
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t t = atomicAdd(J.ticket, 1u);
-        sLast = (t == (uint32_t)(J.nFin - 1)) ? 1 : 0;
-    }
-    __syncthreads();
-    if (!sLast)
+__global__ __launch_bounds__(GATE_THREADS) void serac_gate_many(const Job *__restrict__ jobs,
+                                                                int gatePerJob, Gate G)
+{
+    const Job J = jobs[blockIdx.x / gatePerJob];
+    const int wg = blockIdx.x % gatePerJob;
+    if (wg * GATE_THREADS >= J.nA)
         return;
-    __threadfence();
-    block_exclusive_scan(J.wgcount, J.nFin, sOff);
-    const int all = sOff[J.nFin];
-    for (int p = tid; p < all; p += FIN_THREADS) {
-        // group holding output position p: last k with sOff[k] <= p
-        int lo = 0, hi = J.nFin - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (sOff[mid] <= p)
-                lo = mid;
-            else
-                hi = mid - 1;
+    gate_body(J, wg, G);
+}
+
+// Ordered compaction of one pair by one workgroup: rows are taken 8192 at a
+// time, eight consecutive rows per thread, and a workgroup-wide exclusive
+// scan of the per-thread counts places each thread's matches.  The column
+// accumulators, read by every gate group, are cleared here.
+__device__ __forceinline__ void compact_body(const Job &J)
+{
+    __shared__ int32_t sWave[COMPACT_THREADS / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int32_t run = 0;
+    for (int base = 0; base < J.nA; base += 8 * COMPACT_THREADS) {
+        const int i0 = base + 8 * tid;
+        int32_t v[8];
+        if (i0 + 8 <= J.nA) {
+            const int4 lo = *reinterpret_cast<const int4 *>(J.res + i0);
+            const int4 hi = *reinterpret_cast<const int4 *>(J.res + i0 + 4);
+            v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+            v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                v[k] = (i0 + k < J.nA) ? J.res[i0 + k] : -1;
         }
-        const uint2 m = J.staging[(size_t)lo * FIN_THREADS + (p - sOff[lo])];
-        J.out[p].a = m.x;
-        J.out[p].b = m.y;
+        int32_t cnt = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            cnt += v[k] >= 0;
+        int32_t inc = cnt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int32_t t = __shfl_up(inc, d);
+            if (lane >= d)
+                inc += t;
+        }
+        if (lane == 63)
+            sWave[wv] = inc;
+        __syncthreads();
+        int32_t before = 0, total = 0;
+#pragma unroll
+        for (int k = 0; k < COMPACT_THREADS / 64; ++k) {
+            before += (k < wv) ? sWave[k] : 0;
+            total += sWave[k];
+        }
+        int32_t o = run + before + inc - cnt;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (v[k] >= 0) {
+                J.out[o].a = (uint32_t)(i0 + k);
+                J.out[o].b = (uint32_t)v[k];
+                ++o;
+            }
+        }
+        run += total;
+        __syncthreads();                     // sWave reused by the next tile
     }
-    if (tid == 0) {
-        *J.count = all;
-        *J.ticket = 0u;
-    }
+    for (int j = tid; j < J.nB; j += COMPACT_THREADS)
+        J.cbest[j] = 0ull;
+    if (tid == 0)
+        *J.count = run;
 }
 
-__global__ __launch_bounds__(FIN_THREADS) void serac_finish_one(Job J, Gate G)
+__global__ __launch_bounds__(COMPACT_THREADS) void serac_compact_one(Job J)
 {
-    finish_body(J, blockIdx.x, G);
+    compact_body(J);
 }
 
-__global__ __launch_bounds__(FIN_THREADS) void serac_finish_many(const Job *__restrict__ jobs,
-                                                                 int finPerJob, Gate G)
+__global__ __launch_bounds__(COMPACT_THREADS) void serac_compact_many(const Job *__restrict__ jobs)
 {
-    const Job J = jobs[blockIdx.x / finPerJob];
-    const int wg = blockIdx.x % finPerJob;
-    if (wg >= J.nFin)
-        return;
-    finish_body(J, wg, G);
+    const Job J = jobs[blockIdx.x];
+    compact_body(J);
 }
 
 __global__ void serac_zero_counts(int32_t *const *counts, int32_t *count, int n)
@@ -627,37 +578,48 @@ __global__ void serac_zero_counts(int32_t *const *counts, int32_t *count, int n)
     }
 }
 
-// Export of the row reduction: row_top2[i] = (best, idx, second).
-__global__ void serac_export_rows(Job J, int32_t *row_top2, uint32_t *s1_out)
+// Clears a freshly allocated accumulator buffer (n 16-byte words).
+__global__ void serac_clear(uint4 *p, size_t n)
+{
+    for (size_t k = blockIdx.x * (size_t)blockDim.x + threadIdx.x; k < n;
+         k += (size_t)gridDim.x * blockDim.x)
+        p[k] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Export of the row reduction: row_top2[i] = (best, idx, second).  The best
+// score is kept in rsec for the column export, rbest is cleared.
+__global__ void serac_export_rows(Job J, int32_t *row_top2)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= J.nA)
         return;
     uint32_t S1, S2;
     int32_t I1;
-    merge_row(J, i, S1, I1, S2);
+    row_result(J, J.rbest[i], J.rsec[i], S1, I1, S2);
     row_top2[3 * (size_t)i] = (int32_t)S1;
     row_top2[3 * (size_t)i + 1] = I1;
     row_top2[3 * (size_t)i + 2] = (int32_t)S2;
-    s1_out[i] = S1;
+    J.rbest[i] = 0ull;
+    J.rsec[i] = S1;
 }
 
 // Export of the column reduction: col_best[j] = (best, lowest row).  The
 // winning 16-row slice is known; its first row reaching the best score is
-// found among the rows whose own best is at least that score.
-__global__ void serac_export_cols(Job J, const uint32_t *s1, int32_t *col_best)
+// found among the rows whose own best is at least that score.  cbest is
+// cleared.
+__global__ void serac_export_cols(Job J, int32_t *col_best)
 {
     const int j = blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= J.nB)
         return;
-    uint32_t C1;
-    int32_t slice;
-    merge_col(J, j, C1, slice);
+    const unsigned long long key = J.cbest[j];
+    const uint32_t C1 = (uint32_t)(key >> 32);
+    const int32_t slice = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
     int32_t idx = -1;
     if (C1 > 0u) {
         const uint8_t *b = J.B + (size_t)j * DIM;
         for (int i = slice * SLICE; i < min(slice * SLICE + SLICE, J.nA); ++i) {
-            if (s1[i] >= C1 && (uint32_t)dot_exact(J.A + (size_t)i * DIM, b) == C1) {
+            if (J.rsec[i] >= C1 && (uint32_t)dot_exact(J.A + (size_t)i * DIM, b) == C1) {
                 idx = i;
                 break;
             }
@@ -665,6 +627,15 @@ __global__ void serac_export_cols(Job J, const uint32_t *s1, int32_t *col_best)
     }
     col_best[2 * (size_t)j] = (int32_t)C1;
     col_best[2 * (size_t)j + 1] = idx;
+    J.cbest[j] = 0ull;
+}
+
+// Clears rsec after the column export has used it.
+__global__ void serac_export_clear(Job J)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < J.nA)
+        J.rsec[i] = 0u;
 }
 
 // ------------------------------------------------------------------ host
@@ -705,6 +676,8 @@ void prof_end(hipStream_t s, int slot)
     std::lock_guard<std::mutex> lock(g_prof_mutex);
     (void)hipEventRecord(g_prof.ev[2 * slot + 1], s);
 }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int hip_fail()
 {
@@ -762,18 +735,50 @@ int device_setup(Device **out)
 
 // Grow-only workspace per (device, stream).  Work on one stream runs in
 // order, so consecutive calls on a stream can share one workspace; calls on
-// different streams get different ones.  Growth frees the old buffer and
-// allocates the new one on the same stream, both stream-ordered.
+// different streams get different ones.  Growth frees the old buffers and
+// allocates new ones on the same stream, both stream-ordered.
+//   acc  the accumulators of the jobs; all zero between calls (each call
+//        clears what it raised), cleared by a kernel when (re)allocated or
+//        after a failed call;
+//   aux  per-call scratch (the job table of a batch).
 struct Workspace {
     int dev;
     hipStream_t stream;
-    uint8_t *ptr;
-    size_t bytes;
+    uint8_t *acc;
+    size_t acc_bytes;
+    uint8_t *aux;
+    size_t aux_bytes;
+    bool dirty;
 };
 std::mutex g_ws_mutex;
 std::vector<Workspace> g_ws;
 
-int get_workspace(hipStream_t stream, size_t bytes, uint8_t **out)
+int grow(uint8_t *&ptr, size_t &have, size_t need, hipStream_t stream, bool clear)
+{
+    if (have >= need && ptr)
+        return SERAC_OK;
+    if (ptr)
+        (void)hipFreeAsync(ptr, stream);
+    ptr = nullptr;
+    have = 0;
+    const size_t want = std::max(align256(need), (size_t)1 << 20);
+    if (hipMallocAsync(reinterpret_cast<void **>(&ptr), want, stream) != hipSuccess) {
+        (void)hipGetLastError();
+        ptr = nullptr;
+        return SERAC_ERR_OUT_OF_MEMORY;
+    }
+    have = want;
+    if (clear) {
+        serac_clear<<<1024, 256, 0, stream>>>(reinterpret_cast<uint4 *>(ptr), want / 16);
+        if (hipGetLastError() != hipSuccess)
+            return SERAC_ERR_HIP;
+    }
+    return SERAC_OK;
+}
+
+// The workspace of the current device and `stream`, with at least the
+// given sizes; returns it locked to the caller's use via *out.
+int get_workspace(hipStream_t stream, size_t acc_bytes, size_t aux_bytes, Workspace **out)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
@@ -783,35 +788,36 @@ int get_workspace(hipStream_t stream, size_t bytes, uint8_t **out)
     for (auto &e : g_ws)
         if (e.dev == dev && e.stream == stream)
             w = &e;
-    if (w && w->bytes >= bytes) {
-        *out = w->ptr;
-        return SERAC_OK;
-    }
     if (!w) {
-        g_ws.push_back(Workspace{dev, stream, nullptr, 0});
+        g_ws.push_back(Workspace{dev, stream, nullptr, 0, nullptr, 0, false});
         w = &g_ws.back();
     }
-    if (w->ptr)
-        (void)hipFreeAsync(w->ptr, stream);
-    w->ptr = nullptr;
-    w->bytes = 0;
-    const size_t want = std::max(bytes, (size_t)1 << 20);
-    if (hipMallocAsync(reinterpret_cast<void **>(&w->ptr), want, stream) != hipSuccess) {
-        (void)hipGetLastError();
-        w->ptr = nullptr;
-        return SERAC_ERR_OUT_OF_MEMORY;
+    int st = grow(w->acc, w->acc_bytes, acc_bytes, stream, true);
+    if (st == SERAC_OK && w->dirty) {
+        serac_clear<<<1024, 256, 0, stream>>>(reinterpret_cast<uint4 *>(w->acc),
+                                              w->acc_bytes / 16);
+        st = hipGetLastError() == hipSuccess ? SERAC_OK : SERAC_ERR_HIP;
+        if (st == SERAC_OK)
+            w->dirty = false;
     }
-    w->bytes = want;
-    *out = w->ptr;
-    return SERAC_OK;
+    if (st == SERAC_OK && aux_bytes)
+        st = grow(w->aux, w->aux_bytes, aux_bytes, stream, false);
+    *out = w;
+    return st;
+}
+
+// A call that enqueued work on the accumulators and then failed may have
+// left them raised: have the next call clear them first.
+void mark_dirty(Workspace *w)
+{
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    w->dirty = true;
 }
 
 struct Plan {
-    int nRB, nCC, rbPer, ccPer, Gr, Gc, nFin;
-    size_t rowpart, colpart, staging, wgcount;   // bytes
+    int nRB, nCC, rbPer, ccPer, Gr, Gc;
+    size_t acc;   // bytes of accumulators
 };
-
-size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Choose how many 256 x 512 sub-tiles each workgroup sweeps so that about
 // `target` workgroups cover the pair.
@@ -837,21 +843,12 @@ Plan make_plan(int nA, int nB, int target)
     }
     p.Gr = (p.nRB + p.rbPer - 1) / p.rbPer;
     p.Gc = (p.nCC + p.ccPer - 1) / p.ccPer;
-    p.nFin = (nA + FIN_THREADS - 1) / FIN_THREADS;
-    p.rowpart = align256((size_t)p.Gc * nA * sizeof(int4));
-    p.colpart = align256((size_t)p.Gr * nB * sizeof(uint32_t));
-    p.staging = align256((size_t)p.nFin * FIN_THREADS * sizeof(uint2));
-    p.wgcount = align256((size_t)p.nFin * sizeof(int32_t) + 64);   // + ticket
+    p.acc = align256((size_t)nA * 8) + align256((size_t)nA * 4) + align256((size_t)nB * 8);
     return p;
 }
 
-size_t plan_bytes(const Plan &p)
-{
-    return p.rowpart + p.colpart + p.staging + p.wgcount;
-}
-
 void fill_job(Job &J, const Plan &p, const uint8_t *A, int nA, const uint8_t *B, int nB,
-              uint8_t *ws, serac_match *out, int32_t *count)
+              uint8_t *acc, int32_t *res, serac_match *out, int32_t *count)
 {
     J.A = A;
     J.B = B;
@@ -863,17 +860,13 @@ void fill_job(Job &J, const Plan &p, const uint8_t *A, int nA, const uint8_t *B,
     J.ccPer = p.ccPer;
     J.Gr = p.Gr;
     J.Gc = p.Gc;
-    J.nFin = p.nFin;
-    J.pad = 0;
-    uint8_t *q = ws;
-    J.rowpart = reinterpret_cast<int4 *>(q);
-    q += p.rowpart;
-    J.colpart = reinterpret_cast<uint32_t *>(q);
-    q += p.colpart;
-    J.staging = reinterpret_cast<uint2 *>(q);
-    q += p.staging;
-    J.wgcount = reinterpret_cast<int32_t *>(q);
-    J.ticket = reinterpret_cast<uint32_t *>(q + p.wgcount - 64);
+    uint8_t *q = acc;
+    J.rbest = reinterpret_cast<unsigned long long *>(q);
+    q += align256((size_t)nA * 8);
+    J.rsec = reinterpret_cast<uint32_t *>(q);
+    q += align256((size_t)nA * 4);
+    J.cbest = reinterpret_cast<unsigned long long *>(q);
+    J.res = res;
     J.out = out;
     J.count = count;
 }
@@ -948,12 +941,13 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int
         return hipGetLastError() == hipSuccess ? SERAC_OK : SERAC_ERR_HIP;
     }
     const Plan p = make_plan(nA, nB, d->cus);
-    uint8_t *ws = nullptr;
-    st = get_workspace(stream, plan_bytes(p), &ws);
+    Workspace *w = nullptr;
+    st = get_workspace(stream, p.acc, (size_t)nA * 4, &w);
     if (st != SERAC_OK)
         return st;
     Job J;
-    fill_job(J, p, descA, nA, descB, nB, ws, out->matches, out->count);
+    fill_job(J, p, descA, nA, descB, nB, w->acc, reinterpret_cast<int32_t *>(w->aux),
+             out->matches, out->count);
     const Gate G = make_gate(d, params);
     const int slot = prof_begin(stream);
     if (params->cross_check)
@@ -961,8 +955,13 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int
     else
         serac_tiles_one<false><<<p.Gr * p.Gc, THREADS, 0, stream>>>(J);
     prof_end(stream, slot);
-    serac_finish_one<<<p.nFin, FIN_THREADS, 0, stream>>>(J, G);
-    return hipGetLastError() == hipSuccess ? SERAC_OK : SERAC_ERR_HIP;
+    serac_gate_one<<<(nA + GATE_THREADS - 1) / GATE_THREADS, GATE_THREADS, 0, stream>>>(J, G);
+    serac_compact_one<<<1, COMPACT_THREADS, 0, stream>>>(J);
+    if (hipGetLastError() != hipSuccess) {
+        mark_dirty(w);
+        return SERAC_ERR_HIP;
+    }
+    return SERAC_OK;
 }
 
 int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_images,
@@ -1006,38 +1005,37 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
     const int nlive = (int)live.size();
     const int target = nlive ? std::max(1, (4 * d->cus + nlive - 1) / nlive) : 1;
     std::vector<Plan> plans(nlive);
-    size_t bytes = align256(sizeof(Job) * (size_t)std::max(nlive, 1)) +
-                   align256(sizeof(int32_t *) * zero.size() + 8);
-    int wgPerJob = 1, finPerJob = 1;
+    size_t acc_bytes = 0, res_bytes = 0;
+    int wgPerJob = 1, gatePerJob = 1;
     for (int k = 0; k < nlive; ++k) {
         const serac_pair pr = pairs[live[k]];
         plans[k] = make_plan(n[pr.a], n[pr.b], target);
-        bytes += plan_bytes(plans[k]);
+        acc_bytes += plans[k].acc;
+        res_bytes += align256((size_t)n[pr.a] * 4);
         wgPerJob = std::max(wgPerJob, plans[k].Gr * plans[k].Gc);
-        finPerJob = std::max(finPerJob, plans[k].nFin);
+        gatePerJob = std::max(gatePerJob, (n[pr.a] + GATE_THREADS - 1) / GATE_THREADS);
     }
-    uint8_t *ws = nullptr;
-    st = get_workspace(stream, bytes, &ws);
+    const size_t jobs_bytes = align256(sizeof(Job) * (size_t)std::max(nlive, 1));
+    std::vector<uint8_t> host(jobs_bytes + align256(sizeof(int32_t *) * zero.size() + 8));
+    Workspace *w = nullptr;
+    st = get_workspace(stream, acc_bytes, host.size() + res_bytes, &w);
     if (st != SERAC_OK)
         return st;
-    std::vector<uint8_t> host(align256(sizeof(Job) * (size_t)std::max(nlive, 1)) +
-                              align256(sizeof(int32_t *) * zero.size() + 8));
     Job *jobs = reinterpret_cast<Job *>(host.data());
-    int32_t **zp = reinterpret_cast<int32_t **>(host.data() +
-                                                align256(sizeof(Job) * (size_t)std::max(nlive, 1)));
-    uint8_t *q = ws + host.size();
+    int32_t **zp = reinterpret_cast<int32_t **>(host.data() + jobs_bytes);
+    uint8_t *q = w->acc, *rq = w->aux + host.size();
     for (int k = 0; k < nlive; ++k) {
         const serac_pair pr = pairs[live[k]];
         fill_job(jobs[k], plans[k], desc[pr.a], n[pr.a], desc[pr.b], n[pr.b], q,
-                 out[live[k]].matches, out[live[k]].count);
-        q += plan_bytes(plans[k]);
+                 reinterpret_cast<int32_t *>(rq), out[live[k]].matches, out[live[k]].count);
+        q += plans[k].acc;
+        rq += align256((size_t)n[pr.a] * 4);
     }
     for (size_t k = 0; k < zero.size(); ++k)
         zp[k] = zero[k];
-    hipError_t e = hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, stream);
-    const Job *djobs = reinterpret_cast<const Job *>(ws);
-    int32_t *const *dzero = reinterpret_cast<int32_t *const *>(
-        ws + align256(sizeof(Job) * (size_t)std::max(nlive, 1)));
+    hipError_t e = hipMemcpyAsync(w->aux, host.data(), host.size(), hipMemcpyHostToDevice, stream);
+    const Job *djobs = reinterpret_cast<const Job *>(w->aux);
+    int32_t *const *dzero = reinterpret_cast<int32_t *const *>(w->aux + jobs_bytes);
     if (e == hipSuccess && !zero.empty())
         serac_zero_counts<<<((int)zero.size() + 255) / 256, 256, 0, stream>>>(dzero, nullptr,
                                                                          (int)zero.size());
@@ -1049,7 +1047,8 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
         else
             serac_tiles_many<false><<<nlive * wgPerJob, THREADS, 0, stream>>>(djobs, wgPerJob);
         prof_end(stream, slot);
-        serac_finish_many<<<nlive * finPerJob, FIN_THREADS, 0, stream>>>(djobs, finPerJob, G);
+        serac_gate_many<<<nlive * gatePerJob, GATE_THREADS, 0, stream>>>(djobs, gatePerJob, G);
+        serac_compact_many<<<nlive, COMPACT_THREADS, 0, stream>>>(djobs);
     }
     if (e == hipSuccess)
         e = hipGetLastError();
@@ -1057,7 +1056,11 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
         // the staging buffer `host` must outlive the copy
         e = hipStreamSynchronize(stream);
     }
-    return e == hipSuccess ? SERAC_OK : hip_fail();
+    if (e != hipSuccess) {
+        mark_dirty(w);
+        return hip_fail();
+    }
+    return SERAC_OK;
 }
 
 int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int32_t nB,
@@ -1074,28 +1077,27 @@ int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int3
     if (nA == 0 && nB == 0)
         return SERAC_OK;
     const Plan p = make_plan(std::max(nA, 1), std::max(nB, 1), d->cus);
-    size_t bytes = plan_bytes(p) + align256((size_t)std::max(nA, 1) * sizeof(uint32_t));
-    uint8_t *ws = nullptr;
-    st = get_workspace(stream, bytes, &ws);
+    Workspace *w = nullptr;
+    st = get_workspace(stream, p.acc, 0, &w);
     if (st != SERAC_OK)
         return st;
     Job J;
-    fill_job(J, p, descA, nA, descB, nB, ws, nullptr, nullptr);
-    uint32_t *s1 = reinterpret_cast<uint32_t *>(ws + plan_bytes(p));
+    fill_job(J, p, descA, nA, descB, nB, w->acc, nullptr, nullptr, nullptr);
+    // with an empty side nothing is raised: rows report (0, -1, 0) and
+    // columns (0, -1) from the cleared accumulators
     if (nA > 0 && nB > 0)
         serac_tiles_one<true><<<p.Gr * p.Gc, THREADS, 0, stream>>>(J);
-    // with an empty side the partial tables are never read: rows report
-    // (0, -1, 0) and columns (0, -1) through Gc = Gr = 0
-    Job E = J;
-    if (nA == 0 || nB == 0) {
-        E.Gc = 0;
-        E.Gr = 0;
-    }
     if (nA > 0)
-        serac_export_rows<<<(nA + 255) / 256, 256, 0, stream>>>(E, row_top2, s1);
+        serac_export_rows<<<(nA + 255) / 256, 256, 0, stream>>>(J, row_top2);
     if (nB > 0)
-        serac_export_cols<<<(nB + 255) / 256, 256, 0, stream>>>(E, s1, col_best);
-    return hipGetLastError() == hipSuccess ? SERAC_OK : SERAC_ERR_HIP;
+        serac_export_cols<<<(nB + 255) / 256, 256, 0, stream>>>(J, col_best);
+    if (nA > 0)
+        serac_export_clear<<<(nA + 255) / 256, 256, 0, stream>>>(J);
+    if (hipGetLastError() != hipSuccess) {
+        mark_dirty(w);
+        return SERAC_ERR_HIP;
+    }
+    return SERAC_OK;
 }
 
 int serac_profile_start(int32_t max_launches)
