@@ -128,11 +128,17 @@ __device__ __forceinline__ v4i to_i8(uint4 v)
     return r;
 }
 
-// Byte offset of 16-byte part `part` of column `col` in the LDS chunk.  The
-// XOR spreads eight consecutive columns over distinct bank groups.
+// LDS layout of a chunk: eight planes, one per 16-byte part of the
+// descriptors, each holding that part of all 512 columns back to back.  A
+// wave's 32-column MFMA operand read is then 512 contiguous bytes per lane
+// half; the 32-byte pad per plane keeps the staging writes (four parts of
+// four columns per 16 lanes) on distinct banks.
+constexpr int PLANE = CHUNK * 16 + 32;
+constexpr int CHUNK_LDS = 8 * PLANE;
+
 __device__ __forceinline__ int lds_off(int col, int part)
 {
-    return col * DIM + ((part ^ (col & 7)) << 4);
+    return part * PLANE + col * 16;
 }
 
 // A quarter of a chunk of B (SUB columns) in flight from global memory:
@@ -196,7 +202,7 @@ __device__ __forceinline__ void store_sub(const SubRegs &r, int col0, int t0, ui
 template <bool COLS>
 __device__ __forceinline__ void tiles_body(const Job &J, int wgi)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t sB[2][CHUNK * DIM];   // 2 x 64 KiB
+    __shared__ __attribute__((aligned(16))) uint8_t sB[2][CHUNK_LDS];   // 2 x 64.25 KiB
     __shared__ uint32_t sP[2][CHUNK];
     __shared__ uint32_t sCol[COLS ? MAX_CC_PER_WG * CHUNK : 1];
 
@@ -280,42 +286,69 @@ __device__ __forceinline__ void tiles_body(const Job &J, int wgi)
             const uint32_t *curP = sP[buf];
             uint32_t *colbase = sCol + (COLS ? (cc - cc0) * CHUNK : 0);
 
-#pragma unroll 1
-            for (int sq = 0; sq < NSUB; ++sq) {
-                SubRegs nq;
-                if (pre)
-                    nq = load_sub(J.B, nB, ncc * CHUNK + sq * SUB, tid);
+            // pipeline over the chunk's 8 pairs of 32-column tiles: step p
+            // loads the B operands of pair p + 1 while it runs the MFMAs and
+            // the VALU epilogue of pair p, so LDS latency is covered by a
+            // whole step (the other wave on the SIMD overlaps MFMA and VALU).
+            v4i bf[2][2][4];           // [pair parity][tile][k chunk]
+            uint32_t pp[2][2];         // [pair parity][tile] key addends
+            v16i acc[1][2];            // [tile]
+            SubRegs nq;
+            auto load_pair = [&](int pr, int slot) {
 #pragma unroll
-                for (int up = 0; up < SUB / 64; ++up) {
-                    const int col0 = sq * SUB + up * 64 + n, col1 = col0 + 32;
-                    const uint32_t P0 = curP[col0], P1 = curP[col1];
-                    v16i acc0 = ci, acc1 = ci;
+                for (int t = 0; t < 2; ++t) {
+                    const int col = pr * 64 + 32 * t + n;
+                    pp[slot][t] = curP[col];
 #pragma unroll
-                    for (int kc = 0; kc < 4; ++kc) {
-                        const v4i bf0 = *reinterpret_cast<const v4i *>(curB + lds_off(col0, 2 * kc + h));
-                        const v4i bf1 = *reinterpret_cast<const v4i *>(curB + lds_off(col1, 2 * kc + h));
-                        acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[kc], bf0, acc0, 0, 0, 0);
-                        acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[kc], bf1, acc1, 0, 0, 0);
-                    }
-
-                    uint32_t cm0 = 0u, cm1 = 0u;
+                    for (int kc = 0; kc < 4; ++kc)
+                        bf[slot][t][kc] =
+                            *reinterpret_cast<const v4i *>(curB + lds_off(col, 2 * kc + h));
+                }
+            };
+            auto mfma_pair = [&](int slot) {
 #pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) {
-                        const uint32_t k0 = ((uint32_t)acc0[rr] << 9) + P0;
-                        const uint32_t k1 = ((uint32_t)acc1[rr] << 9) + P1;
-                        const uint32_t md = umed3(b1[rr], k0, k1);
-                        b1[rr] = umax3(b1[rr], k0, k1);
-                        b2[rr] = max(b2[rr], md);
-                        if (COLS) {
-                            cm0 = max(cm0, k0);
-                            cm1 = max(cm1, k1);
-                        }
-                    }
+                for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        acc[0][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                            af[kc], bf[slot][t][kc], kc == 0 ? ci : acc[0][t], 0, 0, 0);
+                }
+            };
+            auto epi_pair = [&](int pr, int slot) {
+                const uint32_t P0 = pp[slot][0], P1 = pp[slot][1];
+                uint32_t cm0 = 0u, cm1 = 0u;
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const uint32_t k0 = ((uint32_t)acc[0][0][rr] << 9) + P0;
+                    const uint32_t k1 = ((uint32_t)acc[0][1][rr] << 9) + P1;
+                    const uint32_t md = umed3(b1[rr], k0, k1);
+                    b1[rr] = umax3(b1[rr], k0, k1);
+                    b2[rr] = max(b2[rr], md);
                     if (COLS) {
-                        atomicMax(colbase + col0, (cm0 & ~511u) | tag);
-                        atomicMax(colbase + col1, (cm1 & ~511u) | tag);
+                        cm0 = max(cm0, k0);
+                        cm1 = max(cm1, k1);
                     }
                 }
+                if (COLS) {
+                    const int col0 = pr * 64 + n;
+                    atomicMax(colbase + col0, (cm0 & ~511u) | tag);
+                    atomicMax(colbase + col0 + 32, (cm1 & ~511u) | tag);
+                }
+            };
+
+            load_pair(0, 0);
+#pragma unroll 1
+            for (int sq = 0; sq < NSUB; ++sq) {
+                // two pairs per quarter: the even one in slot 0, the odd in 1
+                if (pre)
+                    nq = load_sub(J.B, nB, ncc * CHUNK + sq * SUB, tid);
+                load_pair(2 * sq + 1, 1);
+                mfma_pair(0);
+                epi_pair(2 * sq, 0);
+                if (sq + 1 < NSUB)
+                    load_pair(2 * sq + 2, 0);
+                mfma_pair(1);
+                epi_pair(2 * sq + 1, 1);
                 if (pre)
                     store_sub(nq, sq * SUB, nrb == rb ? (ncc - cc0) * (CHUNK / 32) : 0,
                               sB[buf ^ 1], sP[buf ^ 1], tid);
