@@ -15,6 +15,10 @@ HIPCC_FLAGS = [
     "-ffp-contract=off",
     # keep the compiler from forming packed-FP32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # run LLVM's machine-code verifier after every backend pass, so that a
+    # register-allocation inconsistency fails the build instead of producing
+    # a kernel that computes wrong results
+    "-mllvm", "-verify-machineinstrs",
 ]
 
 

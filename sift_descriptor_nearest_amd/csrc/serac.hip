@@ -18,25 +18,38 @@
 //     every term exact in int32 (|sum a'b'| <= 2^21, S < 2^23).
 //     The row term 128*SA_i - 2^21 enters through the MFMA accumulator input,
 //     so it costs no vector instruction.
-//   * A wave keeps the operand fragments of 64 rows of A in registers and
-//     sweeps 32-column tiles of B staged in LDS (512 columns per chunk).
-//     Each score becomes one packed 32-bit key
-//       key = (S << 9) | (511 - local column),
-//     in one v_lshl_add (the column term 128*SB_j is folded into the addend),
-//     and a key comparison orders by score, then by lowest column.  Scores
-//     stay below 2^23, so the key is exact.
-//   * Row top-2: per lane and row, max3/med3 over two new keys at a time.
-//     Keys are unique per column, so a tie on score leaves the tied score in
-//     second place (multiplicity) and the lowest column in first.
+//   * A preparation kernel converts each set once per call into the layouts
+//     the tile kernel reads: A as per-lane MFMA operand fragments plus the
+//     row terms, B as 256-column chunks of eight 16-byte "planes" plus each
+//     column's key addend.  The tile kernel then streams B chunks straight
+//     from global memory into LDS (global_load_lds_dwordx4: no registers,
+//     no vector instructions) two chunks ahead of use.
+//   * A workgroup is four waves, one per SIMD, 128 rows of A by up to 2048
+//     columns of B; two workgroups share a CU.  Each wave keeps the operand
+//     fragments of its 32 rows in registers and sweeps 32-column tiles two at
+//     a time, software-pipelined: the MFMAs of one tile pair are issued while
+//     the vector epilogue of the previous pair runs in the same wave, so the
+//     matrix core and the vector ALU work side by side.
+//   * Each score becomes one packed 32-bit key
+//       key = (S << 9) | (511 - t),
+//     t being the index of its 32-column tile in the 2048-column window, in
+//     one v_lshl_add (the column term 128*SB_j is folded into the addend).
+//     A key comparison orders by score, then by lowest column.  Scores stay
+//     below 2^23, so the key is exact.
+//   * Row top-2: per lane and row, max3/med3 over two new keys at a time; the
+//     second-best update is deferred to every other pair (the runner-up of
+//     the two pairs is folded in with one max3).  Keys are unique per column,
+//     so a tie on score leaves the tied score in second place (multiplicity)
+//     and the lowest column in first.
 //   * Column best: a max3 tree over the 16 rows a lane holds in one tile
 //     gives the column maximum of those rows; the key's low 9 bits are then
 //     replaced by the 16-row slice number (lowest slice wins) and merged with
 //     an LDS atomic max.  The exact lowest row inside the winning slice is
 //     settled afterwards from the 15 rows that precede it (rarely more than
 //     a filter check).
-//   * All merges (across lanes, waves, chunks, workgroups) compare packed
-//     keys or scan in ascending index order, so the result does not depend
-//     on scheduling (MASDA part 3, section 6: an order-independent key).
+//   * All merges (across lanes, waves, workgroups) compare packed keys or
+//     scan in ascending index order, so the result does not depend on
+//     scheduling (MASDA part 3, section 6: an order-independent key).
 //   * The angle gate reads a table of acos(s / 512^2) built on the host with
 //     the C library's acos, so the double-precision decision is the same
 //     one a CPU makes; the ratio test is one IEEE multiply and compare.
@@ -48,6 +61,7 @@
 #include <cstring>
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "serac.h"
@@ -55,15 +69,16 @@
 namespace {
 
 constexpr int DIM = 128;
-constexpr int THREADS = 512;            // 8 waves of 64
-constexpr int ROWS_PER_WAVE = 32;       // one 32-row MFMA tile
-constexpr int ROWS_PER_BLOCK = 256;     // rows of A per workgroup pass
+constexpr int TILE_THREADS = 256;       // 4 waves of 64, one per SIMD
+constexpr int WAVE_ROWS = 32;           // one 32-row MFMA tile per wave
+constexpr int BLOCK_ROWS = 128;         // rows of A per workgroup
 constexpr int SLICE = 16;               // rows per column tie-break slice
-constexpr int CHUNK = 512;              // columns of B per LDS chunk (9-bit index)
-constexpr int SUB = 128;                // columns per staged sub-chunk
-constexpr int NSUB = CHUNK / SUB;
-constexpr int MAX_CC_PER_WG = 4;        // chunks one workgroup sweeps
-constexpr int MAX_RB_PER_WG = 32;       // 32 blocks * 16 slices = 512 slice ids
+constexpr int CHUNK = 256;              // columns of B per LDS chunk
+constexpr int CHUNK_BYTES = CHUNK * DIM;
+constexpr int PLANE_BYTES = CHUNK * 16; // one 16-byte part of every column
+constexpr int GROUP_MAX = 2048;         // columns per workgroup: 64 tiles (6-bit index)
+constexpr int MAX_GCH = GROUP_MAX / CHUNK;
+constexpr int PREP_THREADS = 256;
 constexpr int NORM2 = 262144;           // 512^2
 constexpr int GATE_THREADS = 256;
 constexpr int COMPACT_THREADS = 1024;
@@ -71,16 +86,42 @@ constexpr int COMPACT_THREADS = 1024;
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
+// One set prepared for the tile kernel (either role or both).
+//   Af  [rowsA/128][4 waves][4 k-slices][64 lanes][16 B]: the MFMA A operand
+//       of every lane, bytes a ^ 0x80.  Lane (n, h) of wave w holds bytes
+//       [32*kc + 16*h, +16) of wave row q(n) = 16*((n>>2)&1) + 4*(n>>3) + n%4.
+//   RT  [rowsA] row term 128*SA - 2^21.
+//   Bp  [rowsB/256][8 parts][256 columns][16 B]: part p of column j holds
+//       bytes [16*p, +16) of that descriptor, ^ 0x80.
+//   P   [rowsB] key addend ((128*SB) << 9) + (511 - ((j >> 5) & 63)).
+// Rows beyond n are all-zero descriptors: their score against anything is 0.
+struct PrepJob {
+    const uint8_t *X;
+    int32_t n;
+    int32_t rowsA, rowsB;    // padded row counts of the two roles (0 = role unused)
+    uint8_t *Af;
+    int32_t *RT;
+    uint8_t *Bp;
+    uint32_t *P;
+};
+
+struct PrepPair {
+    PrepJob q[2];
+};
+
 // One pair's work description and its accumulators.  The accumulators
 // are zero between calls: the tile kernel raises them with atomic maxima and
-// the finishing kernel reads them and clears them again.
+// the finishing kernels read them and clear them again.
 struct Job {
-    const uint8_t *A;
+    const uint8_t *A;        // raw descriptors (exact tie checks)
     const uint8_t *B;
+    const uint8_t *Af;       // prepared A (see PrepJob)
+    const int32_t *RT;
+    const uint8_t *Bp;       // prepared B
+    const uint32_t *P;
     int32_t nA, nB;
-    int32_t nRB, nCC;        // row blocks of 256, column chunks of 512
-    int32_t rbPer, ccPer;    // per workgroup
-    int32_t Gr, Gc;          // workgroup grid (row groups x column groups)
+    int32_t nRB, nBC;        // 128-row blocks of A, 256-column chunks of B
+    int32_t gch, Gc;         // chunks per workgroup (1, 2, 4 or 8), column groups
     unsigned long long *rbest;  // [nA] (best << 32) | ~column   (max: lowest column)
     uint32_t *rsec;             // [nA] second-best score
     unsigned long long *cbest;  // [nB] (best << 32) | ~slice    (max: lowest slice)
@@ -118,303 +159,324 @@ __device__ __forceinline__ uint32_t bytesum16(uint4 v)
     return __builtin_amdgcn_udot4(v.w, 0x01010101u, s, false);
 }
 
-__device__ __forceinline__ v4i to_i8(uint4 v)
+// Wait until at most `n` vector-memory loads of this wave are outstanding
+// (gfx9 s_waitcnt encoding; exp and lgkm counters left alone).  Loads
+// complete in issue order, so this waits for all but the last n issued.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
 {
-    v4i r;
-    r[0] = (int)(v.x ^ 0x80808080u);
-    r[1] = (int)(v.y ^ 0x80808080u);
-    r[2] = (int)(v.z ^ 0x80808080u);
-    r[3] = (int)(v.w ^ 0x80808080u);
-    return r;
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// LDS layout of a chunk: eight planes, one per 16-byte part of the
-// descriptors, each holding that part of all 512 columns back to back.  A
-// wave's 32-column MFMA operand read is then 512 contiguous bytes per lane
-// half; the 32-byte pad per plane keeps the staging writes (four parts of
-// four columns per 16 lanes) on distinct banks.
-constexpr int PLANE = CHUNK * 16 + 32;
-constexpr int CHUNK_LDS = 8 * PLANE;
+typedef __attribute__((address_space(3))) void *lds_void_ptr;
 
-__device__ __forceinline__ int lds_off(int col, int part)
+// 16 bytes per lane from global memory straight into LDS: lane l of the
+// wave writes bytes [16*l, 16*l + 16) after `lds_wave_base`, which must be
+// the same for the whole wave.
+__device__ __forceinline__ void load_lds16(const void *src, void *lds_wave_base)
 {
-    return part * PLANE + col * 16;
+    __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)lds_wave_base, 16, 0, 0);
 }
 
-// A quarter of a chunk of B (SUB columns) in flight from global memory:
-// each thread holds 32 bytes (a quarter) of one column.
-struct SubRegs {
-    uint4 lo, hi;
-};
+// ------------------------------------------------------------ preparation
 
-__device__ __forceinline__ SubRegs load_sub(const uint8_t *__restrict__ B, int nB, int gcol0,
-                                            int tid)
+// Converts one set: one thread per (row, 16-byte part), eight threads per
+// row in consecutive lanes.
+__device__ __forceinline__ void prep_body(const PrepJob &Q, int blk)
 {
-    const int col = tid >> 2, q = tid & 3;
-    const int gcol = gcol0 + col;
-    SubRegs r;
-    r.lo = make_uint4(0u, 0u, 0u, 0u);
-    r.hi = r.lo;
-    if (gcol < nB) {
-        const uint8_t *p = B + (size_t)gcol * DIM + q * 32;
-        r.lo = *reinterpret_cast<const uint4 *>(p);
-        r.hi = *reinterpret_cast<const uint4 *>(p + 16);
-    }
-    return r;
-}
-
-// Write a quarter chunk into LDS as int8 (a ^ 0x80) at chunk columns
-// [col0, col0 + SUB), with each column's key addend
-//   P = ((128 * SB) << 9) + (511 - t),
-// t being the index of the column's 32-column tile among the tiles this
-// workgroup sweeps (t0 = index of the chunk's first tile).
-__device__ __forceinline__ void store_sub(const SubRegs &r, int col0, int t0, uint8_t *sB,
-                                          uint32_t *sP, int tid)
-{
-    const int col = col0 + (tid >> 2), q = tid & 3;
-    uint32_t s = bytesum16(r.lo) + bytesum16(r.hi);
+    const int t = blk * PREP_THREADS + (int)threadIdx.x;
+    const int r = t >> 3, part = t & 7;
+    if (r >= max(Q.rowsA, Q.rowsB))
+        return;                              // whole rows (rows are multiples of 128)
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < Q.n)
+        v = *reinterpret_cast<const uint4 *>(Q.X + (size_t)r * DIM + 16 * part);
+    uint32_t s = bytesum16(v);
     s += __shfl_xor(s, 1);
     s += __shfl_xor(s, 2);
-    if (q == 0)
-        sP[col] = ((s * 128u) << 9) + (uint32_t)(511 - (t0 + (col >> 5)));
-    *reinterpret_cast<v4i *>(sB + lds_off(col, 2 * q)) = to_i8(r.lo);
-    *reinterpret_cast<v4i *>(sB + lds_off(col, 2 * q + 1)) = to_i8(r.hi);
+    s += __shfl_xor(s, 4);
+    const uint4 x = make_uint4(v.x ^ 0x80808080u, v.y ^ 0x80808080u, v.z ^ 0x80808080u,
+                               v.w ^ 0x80808080u);
+    if (r < Q.rowsA) {
+        const int b = r >> 7, w = (r >> 5) & 3, qr = r & 31;
+        const int nn = 8 * ((qr >> 2) & 3) + 4 * (qr >> 4) + (qr & 3);   // q(nn) = qr
+        const int kc = part >> 1, hh = part & 1;
+        const size_t off = ((((size_t)b * 4 + w) * 4 + kc) * 64 + 32 * hh + nn) * 16;
+        *reinterpret_cast<uint4 *>(Q.Af + off) = x;
+        if (part == 0)
+            Q.RT[r] = (int32_t)(128u * s) - 2097152;
+    }
+    if (r < Q.rowsB) {
+        const int c = r >> 8, j = r & 255;
+        const size_t off = (((size_t)c * 8 + part) * CHUNK + j) * 16;
+        *reinterpret_cast<uint4 *>(Q.Bp + off) = x;
+        if (part == 0)
+            Q.P[r] = ((128u * s) << 9) + (uint32_t)(511 - ((r >> 5) & 63));
+    }
 }
 
-// The fused tile sweep of one workgroup: row blocks [rb0, rb1) of 256 rows
-// by column chunks [cc0, cc1) of 512 columns.  Each of the 8 waves owns 32
-// rows as one tile of v_mfma_i32_32x32x32_i8 (on gfx950 this MFMA leaves the
-// vector ALU free far more of the time than the 16x16x64 form does).  B is
-// double-buffered in LDS: while one chunk is swept, the next one (of this
-// row block, or the first of the next row block) is loaded a quarter at a
-// time into the other buffer.
+__global__ __launch_bounds__(PREP_THREADS) void serac_prep_pair(PrepPair Q)
+{
+    prep_body(Q.q[blockIdx.y], blockIdx.x);
+}
+
+__global__ __launch_bounds__(PREP_THREADS) void serac_prep_many(const PrepJob *__restrict__ Q)
+{
+    prep_body(Q[blockIdx.y], blockIdx.x);
+}
+
+// ------------------------------------------------------------ tile sweep
+
+// The fused sweep of one workgroup: 128 rows of A (row block rb) against
+// chunks [c0, c0 + nch) of B.
 //
 // Accumulator layout of the 32x32 MFMA: lane l, register r holds output row
 // 8*(r/4) + 4*(l/32) + r%4 of column l%32.  The operand row that feeds
-// output row m is wave row 16*((m/4)%2) + 4*(m/8) + m%4, so lane half h,
-// register r is wave row 16*h + r: each lane half covers 16 consecutive
+// output row m is wave row q(m) = 16*((m/4)%2) + 4*(m/8) + m%4, so lane half
+// h, register r is wave row 16*h + r: each lane half covers 16 consecutive
 // rows (one column tie-break slice).
 //
-// A lane only ever sees columns l%32 + 32*t of its workgroup's range, so
-// its running top-2 keys carry t (at most 64 tiles) in their low 9 bits and
-// stay valid across chunks; the 32 lanes sharing a row are merged once per
-// row block.
+// A lane only ever sees columns l%32 + 32*t of the workgroup's range, so
+// its running top-2 keys carry t in their low 9 bits and stay valid across
+// chunks; the 32 lanes sharing a row are merged once at the end.
+//
+// Schedule per chunk (4 tile pairs, k = 0..3): step k issues the MFMAs of
+// pair k, runs the epilogue of pair k-1 (pair 3 of the previous chunk for
+// k = 0) and reads the operands of pair k+1 from LDS; the accumulators and
+// operands alternate between two register sets.  Chunk c+2 is fetched into
+// LDS while chunks c and c+1 are in use.
 template <bool COLS>
-__device__ __forceinline__ void tiles_body(const Job &J, int wgi)
+__device__ __forceinline__ void tiles_body(const Job &J, int u)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t sB[2][CHUNK_LDS];   // 2 x 64.25 KiB
-    __shared__ uint32_t sP[2][CHUNK];
-    __shared__ uint32_t sCol[COLS ? MAX_CC_PER_WG * CHUNK : 1];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[2 * CHUNK_BYTES];   // 64 KiB
+    __shared__ __attribute__((aligned(16))) uint32_t sP[2 * CHUNK];
+    __shared__ uint32_t sCol[COLS ? GROUP_MAX : 1];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, h = lane >> 5;
-    const int r = wgi % J.Gr, c = wgi / J.Gr;
-    const int rb0 = r * J.rbPer, rb1 = min(rb0 + J.rbPer, J.nRB);
-    const int cc0 = c * J.ccPer, cc1 = min(cc0 + J.ccPer, J.nCC);
-    if (rb0 >= rb1 || cc0 >= cc1)
-        return;
-    const int nA = J.nA, nB = J.nB;
-    const int nchunks = cc1 - cc0;
+    const int rb = u % J.nRB, cg = u / J.nRB;
+    const int c0 = cg * J.gch;
+    const int nch = min(J.gch, J.nBC - c0);
 
+    // ---- this wave's rows of A: operand fragments and the row terms
+    v4i af[4];
+    v16i ci;
+    {
+        const v4i *pa = reinterpret_cast<const v4i *>(J.Af) + (size_t)(rb * 4 + w) * 256 + lane;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+            af[kc] = pa[64 * kc];
+        const v4i *pr = reinterpret_cast<const v4i *>(J.RT + rb * BLOCK_ROWS + w * WAVE_ROWS +
+                                                      16 * h);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const v4i x = pr[g];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ci[4 * g + e] = x[e];
+        }
+    }
+
+    // ---- chunk staging: 8 + (wave 0) 1 loads per thread
+    auto stage = [&](int c, int buf) {
+        const uint8_t *src = J.Bp + (size_t)(c0 + c) * CHUNK_BYTES + tid * 16;
+        uint8_t *dst = sB + buf * CHUNK_BYTES + w * 1024;
+#pragma unroll
+        for (int k = 0; k < CHUNK_BYTES / (TILE_THREADS * 16); ++k)
+            load_lds16(src + k * (TILE_THREADS * 16), dst + k * (TILE_THREADS * 16));
+        if (w == 0)
+            load_lds16(J.P + (size_t)(c0 + c) * CHUNK + lane * 4, sP + buf * CHUNK);
+    };
+    stage(0, 0);
+    if (nch > 1)
+        stage(1, 1);
     if (COLS) {
-        for (int k = tid; k < nchunks * CHUNK; k += THREADS)
+        for (int k = tid; k < nch * CHUNK; k += TILE_THREADS)
             sCol[k] = 0u;
     }
+    if (nch > 1)
+        wait_vmcnt<8>();                     // chunk 0 (and the A loads) landed
+    else
+        wait_vmcnt<0>();
+    __syncthreads();
 
-    // stage the first chunk
-    {
-        SubRegs q[NSUB];
+    v4i bf[2][4];        // [tile][k-slice]: operands of the next pair
+    uint32_t pk[2][2];   // [set][tile] key addends
+    v16i acc[2][2];      // [set][tile]
+    // The running top-2 starts from a zero the compiler cannot see through:
+    // with a literal 0 the gfx950 register coalescer merged one of these
+    // initial values into the zero upper half of a 64-bit address and lost
+    // it (the machine verifier reports "no live subrange at use").
+    uint32_t zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+    uint32_t b1[16], b2[16], tk[16];
 #pragma unroll
-        for (int sq = 0; sq < NSUB; ++sq)
-            q[sq] = load_sub(J.B, nB, cc0 * CHUNK + sq * SUB, tid);
-#pragma unroll
-        for (int sq = 0; sq < NSUB; ++sq)
-            store_sub(q[sq], sq * SUB, 0, sB[0], sP[0], tid);
+    for (int x = 0; x < 16; ++x) {
+        b1[x] = zero;
+        b2[x] = zero;
+        tk[x] = zero;
     }
-    int buf = 0;
+    const uint32_t tag = (uint32_t)(511 - (2 * w + h));
 
-    for (int rb = rb0; rb < rb1; ++rb) {
-        // ---- this wave's 32 rows of A: operand fragments and the row term
-        v4i af[4];
-        v16i ci;
-        {
-            const int m = n;
-            const int q = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
-            const int row = rb * ROWS_PER_BLOCK + w * ROWS_PER_WAVE + q;
-            uint4 x[4];
+    auto frags = [&](int buf, int pr, int set) {
+        const uint8_t *base = sB + buf * CHUNK_BYTES + h * PLANE_BYTES + n * 16 + pr * 1024;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc)
-                x[kc] = make_uint4(0u, 0u, 0u, 0u);
-            if (row < nA) {
-                const uint8_t *a = J.A + (size_t)row * DIM + 16 * h;
-#pragma unroll
-                for (int kc = 0; kc < 4; ++kc)
-                    x[kc] = *reinterpret_cast<const uint4 *>(a + 32 * kc);
-            }
-            uint32_t s = bytesum16(x[0]) + bytesum16(x[1]) + bytesum16(x[2]) + bytesum16(x[3]);
-            s += __shfl_xor(s, 32);
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc)
-                af[kc] = to_i8(x[kc]);
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const int mo = 8 * (rr >> 2) + 4 * h + (rr & 3);
-                ci[rr] = (int)(128u * (uint32_t)__shfl((int)s, mo)) - 2097152;
-            }
+                bf[tt][kc] =
+                    *reinterpret_cast<const v4i *>(base + kc * 2 * PLANE_BYTES + tt * 512);
+            pk[set][tt] = sP[buf * CHUNK + pr * 64 + tt * 32 + n];
         }
-        __syncthreads();                     // the chunk in sB[buf] is complete
-
-        uint32_t b1[16], b2[16];
+    };
+    auto mfma = [&](int set) {
 #pragma unroll
-        for (int x = 0; x < 16; ++x) {
-            b1[x] = 0u;
-            b2[x] = 0u;
+        for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+                acc[set][tt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                    af[kc], bf[tt][kc], kc == 0 ? ci : acc[set][tt], 0, 0, 0);
         }
-        const int slice = (rb - rb0) * (ROWS_PER_BLOCK / SLICE) + w * 2 + h;
-        const uint32_t tag = (uint32_t)(511 - slice);
-
-        for (int cc = cc0; cc < cc1; ++cc) {
-            // the chunk that follows this one in the sweep, if any
-            int ncc = cc + 1, nrb = rb;
-            if (ncc == cc1) {
-                ncc = cc0;
-                nrb = rb + 1;
-            }
-            const bool pre = nrb < rb1;
-            const uint8_t *curB = sB[buf];
-            const uint32_t *curP = sP[buf];
-            uint32_t *colbase = sCol + (COLS ? (cc - cc0) * CHUNK : 0);
-
-            // pipeline over the chunk's 8 pairs of 32-column tiles: step p
-            // loads the B operands of pair p + 1 while it runs the MFMAs and
-            // the VALU epilogue of pair p, so LDS latency is covered by a
-            // whole step (the other wave on the SIMD overlaps MFMA and VALU).
-            v4i bf[2][2][4];           // [pair parity][tile][k chunk]
-            uint32_t pp[2][2];         // [pair parity][tile] key addends
-            v16i acc[1][2];            // [tile]
-            SubRegs nq;
-            auto load_pair = [&](int pr, int slot) {
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int col = pr * 64 + 32 * t + n;
-                    pp[slot][t] = curP[col];
-#pragma unroll
-                    for (int kc = 0; kc < 4; ++kc)
-                        bf[slot][t][kc] =
-                            *reinterpret_cast<const v4i *>(curB + lds_off(col, 2 * kc + h));
-                }
-            };
-            auto mfma_pair = [&](int slot) {
-#pragma unroll
-                for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-                    for (int t = 0; t < 2; ++t)
-                        acc[0][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                            af[kc], bf[slot][t][kc], kc == 0 ? ci : acc[0][t], 0, 0, 0);
-                }
-            };
-            auto epi_pair = [&](int pr, int slot) {
-                const uint32_t P0 = pp[slot][0], P1 = pp[slot][1];
-                uint32_t cm0 = 0u, cm1 = 0u;
-#pragma unroll
-                for (int rr = 0; rr < 16; ++rr) {
-                    const uint32_t k0 = ((uint32_t)acc[0][0][rr] << 9) + P0;
-                    const uint32_t k1 = ((uint32_t)acc[0][1][rr] << 9) + P1;
-                    const uint32_t md = umed3(b1[rr], k0, k1);
-                    b1[rr] = umax3(b1[rr], k0, k1);
-                    b2[rr] = max(b2[rr], md);
-                    if (COLS) {
-                        cm0 = max(cm0, k0);
-                        cm1 = max(cm1, k1);
-                    }
-                }
-                if (COLS) {
-                    const int col0 = pr * 64 + n;
-                    atomicMax(colbase + col0, (cm0 & ~511u) | tag);
-                    atomicMax(colbase + col0 + 32, (cm1 & ~511u) | tag);
-                }
-            };
-
-            load_pair(0, 0);
-#pragma unroll 1
-            for (int sq = 0; sq < NSUB; ++sq) {
-                // two pairs per quarter: the even one in slot 0, the odd in 1
-                if (pre)
-                    nq = load_sub(J.B, nB, ncc * CHUNK + sq * SUB, tid);
-                load_pair(2 * sq + 1, 1);
-                mfma_pair(0);
-                epi_pair(2 * sq, 0);
-                if (sq + 1 < NSUB)
-                    load_pair(2 * sq + 2, 0);
-                mfma_pair(1);
-                epi_pair(2 * sq + 1, 1);
-                if (pre)
-                    store_sub(nq, sq * SUB, nrb == rb ? (ncc - cc0) * (CHUNK / 32) : 0,
-                              sB[buf ^ 1], sP[buf ^ 1], tid);
-            }
-            __syncthreads();                 // next chunk complete, this one free
-            buf ^= 1;
-        }
-
-        // ---- merge the 32 lanes that share each row (via LDS, in the free
-        // buffer): lane pair (q, q + 32) folds 16 of the 32 entries of row q
-        // each; key ties (same score, same tile) go to the lower lane, which
-        // is the lower column.
-        uint2 *scr = reinterpret_cast<uint2 *>(sB[buf ^ 1]) + w * (ROWS_PER_WAVE * 32);
+    };
+    // epilogue of tile pair `pr` of chunk `c`, held in register set `set`;
+    // `odd` pairs close the deferred second-best update
+    auto epi = [&](int set, int c, int pr, auto odd) {
+        uint32_t k0[16], k1[16];
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-            const int q = 16 * h + rr;
-            scr[q * 32 + ((n + q) & 31)] = make_uint2(b1[rr], b2[rr]);
+            k0[rr] = ((uint32_t)acc[set][0][rr] << 9) + pk[set][0];
+            k1[rr] = ((uint32_t)acc[set][1][rr] << 9) + pk[set][1];
         }
-        __syncthreads();
-        uint32_t K1 = 0u, K2 = 0u;
-        int L1 = 64;
+        if (COLS) {
+            uint32_t m0[5], m1[5];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int src = (16 * h + k) & 31;              // source lane (column)
-            const uint2 e = scr[n * 32 + ((src + n) & 31)];
-            const uint32_t lo = min(K1, e.x);
-            if (e.x > K1 || (e.x == K1 && src < L1))
-                L1 = src;
-            K1 = max(K1, e.x);
-            K2 = umax3(lo, K2, e.y);
+            for (int g = 0; g < 5; ++g) {
+                m0[g] = umax3(k0[3 * g], k0[3 * g + 1], k0[3 * g + 2]);
+                m1[g] = umax3(k1[3 * g], k1[3 * g + 1], k1[3 * g + 2]);
+            }
+            const uint32_t cm0 = max(umax3(m0[0], m0[1], m0[2]), umax3(m0[3], m0[4], k0[15]));
+            const uint32_t cm1 = max(umax3(m1[0], m1[1], m1[2]), umax3(m1[3], m1[4], k1[15]));
+            uint32_t *cp = sCol + c * CHUNK + pr * 64 + n;
+            atomicMax(cp, (cm0 & ~511u) | tag);
+            atomicMax(cp + 32, (cm1 & ~511u) | tag);
         }
-        {
-            const uint32_t o1 = __shfl_xor(K1, 32), o2 = __shfl_xor(K2, 32);
-            const int oL = __shfl_xor(L1, 32);
-            const uint32_t lo = min(K1, o1);
-            if (o1 > K1 || (o1 == K1 && oL < L1))
-                L1 = oL;
-            K1 = max(K1, o1);
-            K2 = umax3(lo, K2, o2);
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const uint32_t md = umed3(b1[rr], k0[rr], k1[rr]);
+            b1[rr] = umax3(b1[rr], k0[rr], k1[rr]);
+            if (decltype(odd)::value)
+                b2[rr] = umax3(b2[rr], tk[rr], md);
+            else
+                tk[rr] = md;
         }
-        __syncthreads();                     // scratch free
-        // publish this row block's top-2 over the workgroup's columns: the
-        // atomic max keeps the best key over all workgroups; whichever key
-        // loses an exchange (or this group's own second) raises the row's
-        // second score, so the second ends as the runner-up of all
-        // candidates, ties counted.
-        const uint32_t S1 = K1 >> 9, S2 = K2 >> 9;
-        const int row = rb * ROWS_PER_BLOCK + w * ROWS_PER_WAVE + n;
-        if (h == 0 && row < nA && S1 > 0u) {
-            const uint32_t col = (uint32_t)(cc0 * CHUNK + 32 * (511 - (int)(K1 & 511u)) + L1);
-            const unsigned long long key = ((unsigned long long)S1 << 32) | (0xFFFFFFFFu - col);
-            const unsigned long long old = atomicMax(J.rbest + row, key);
-            const uint32_t loser = (uint32_t)(min(old, key) >> 32);
-            atomicMax(J.rsec + row, max(loser, S2));
+    };
+    using Even = std::integral_constant<bool, false>;
+    using Odd = std::integral_constant<bool, true>;
+
+    // Steps do not mix: each step's MFMAs, epilogue and operand reads are
+    // scheduled among themselves.
+    auto schedule = [&](auto, auto) { __builtin_amdgcn_sched_barrier(0); };
+    using Yes = std::integral_constant<bool, true>;
+    using No = std::integral_constant<bool, false>;
+
+    // chunk c: pairs 1..3 of the chunk and pair 0 of the next one (pair 0
+    // of chunk 0 is issued before the loop)
+    auto chunk = [&](int c) {
+        const int buf = c & 1;
+        mfma(1);
+        epi(0, c, 0, Even{});
+        frags(buf, 2, 0);
+        schedule(Yes{}, Yes{});
+        mfma(0);
+        epi(1, c, 1, Odd{});
+        frags(buf, 3, 1);
+        schedule(Yes{}, Yes{});
+        mfma(1);
+        epi(0, c, 2, Even{});
+        schedule(Yes{}, No{});
+        if (c + 1 < nch) {
+            wait_vmcnt<0>();                 // chunk c+1 landed (this wave's part)
+            __syncthreads();                 // ... all parts; chunk c no longer read
+            if (c + 2 < nch)
+                stage(c + 2, buf);
+            frags(buf ^ 1, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma(0);
+            epi(1, c, 3, Odd{});
+            frags(buf ^ 1, 1, 1);
+            schedule(Yes{}, Yes{});
+        } else {
+            epi(1, c, 3, Odd{});
         }
+    };
+
+    frags(0, 0, 0);
+    mfma(0);
+    frags(0, 1, 1);
+    schedule(No{}, Yes{});
+    for (int c = 0; c < nch; ++c)
+        chunk(c);
+
+    // ---- merge the 32 lanes that share each row (via LDS, in the chunk
+    // buffers, now free): lane pair (q, q + 32) folds 16 of the 32 entries of
+    // row q each; key ties (same score, same tile) go to the lower lane,
+    // which is the lower column.
+    __syncthreads();
+    uint2 *scr = reinterpret_cast<uint2 *>(sB) + w * (WAVE_ROWS * 32);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+        const int q = 16 * h + rr;
+        scr[q * 32 + ((n + q) & 31)] = make_uint2(b1[rr], b2[rr]);
+    }
+    __syncthreads();
+    uint32_t K1 = 0u, K2 = 0u;
+    int L1 = 64;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int src = (16 * h + k) & 31;              // source lane (column)
+        const uint2 e = scr[n * 32 + ((src + n) & 31)];
+        const uint32_t lo = min(K1, e.x);
+        if (e.x > K1 || (e.x == K1 && src < L1))
+            L1 = src;
+        K1 = max(K1, e.x);
+        K2 = umax3(lo, K2, e.y);
+    }
+    {
+        const uint32_t o1 = __shfl_xor(K1, 32), o2 = __shfl_xor(K2, 32);
+        const int oL = __shfl_xor(L1, 32);
+        const uint32_t lo = min(K1, o1);
+        if (o1 > K1 || (o1 == K1 && oL < L1))
+            L1 = oL;
+        K1 = max(K1, o1);
+        K2 = umax3(lo, K2, o2);
+    }
+    // publish this row block's top-2 over the workgroup's columns: the
+    // atomic max keeps the best key over all workgroups; whichever key
+    // loses an exchange (or this group's own second) raises the row's
+    // second score, so the second ends as the runner-up of all
+    // candidates, ties counted.
+    const uint32_t S1 = K1 >> 9, S2 = K2 >> 9;
+    const int row = rb * BLOCK_ROWS + w * WAVE_ROWS + n;
+    if (h == 0 && row < J.nA && S1 > 0u) {
+        const int window = (c0 * CHUNK) & ~(GROUP_MAX - 1);
+        const uint32_t col = (uint32_t)(window + 32 * (511 - (int)(K1 & 511u)) + L1);
+        const unsigned long long key = ((unsigned long long)S1 << 32) | (0xFFFFFFFFu - col);
+        const unsigned long long old = atomicMax(J.rbest + row, key);
+        const uint32_t loser = (uint32_t)(min(old, key) >> 32);
+        atomicMax(J.rsec + row, max(loser, S2));
     }
 
     if (COLS) {
-        __syncthreads();
-        const int base = cc0 * CHUNK;
-        for (int k = tid; k < nchunks * CHUNK; k += THREADS) {
+        // every LDS column maximum was raised before the barriers above
+        const int base = c0 * CHUNK;
+        for (int k = tid; k < nch * CHUNK; k += TILE_THREADS) {
             const int col = base + k;
             const uint32_t key = sCol[k];
-            if (col < nB && (key >> 9) > 0u) {
-                const uint32_t slice = (uint32_t)(r * J.rbPer * (ROWS_PER_BLOCK / SLICE) + 511 -
-                                                  (int)(key & 511u));
+            if (col < J.nB && (key >> 9) > 0u) {
+                const uint32_t slice =
+                    (uint32_t)(rb * (BLOCK_ROWS / SLICE) + 511 - (int)(key & 511u));
                 atomicMax(J.cbest + col,
                           ((unsigned long long)(key >> 9) << 32) | (0xFFFFFFFFu - slice));
             }
@@ -423,20 +485,20 @@ __device__ __forceinline__ void tiles_body(const Job &J, int wgi)
 }
 
 template <bool COLS>
-__global__ __launch_bounds__(THREADS, 1) void serac_tiles_one(Job J)
+__global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_one(Job J)
 {
     tiles_body<COLS>(J, blockIdx.x);
 }
 
 template <bool COLS>
-__global__ __launch_bounds__(THREADS, 1) void serac_tiles_many(const Job *__restrict__ jobs,
-                                                               int wgPerJob)
+__global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_many(const Job *__restrict__ jobs,
+                                                                    int unitsPerJob)
 {
-    const Job J = jobs[blockIdx.x / wgPerJob];
-    const int wgi = blockIdx.x % wgPerJob;
-    if (wgi >= J.Gr * J.Gc)
+    const Job J = jobs[blockIdx.x / unitsPerJob];
+    const int u = blockIdx.x % unitsPerJob;
+    if (u >= J.nRB * J.Gc)
         return;
-    tiles_body<COLS>(J, wgi);
+    tiles_body<COLS>(J, u);
 }
 
 // Exact inner product of two descriptors (used only to settle column ties
@@ -848,50 +910,88 @@ void mark_dirty(Workspace *w)
 }
 
 struct Plan {
-    int nRB, nCC, rbPer, ccPer, Gr, Gc;
+    int nRB, nBC, gch, Gc;
     size_t acc;   // bytes of accumulators
+    int units() const { return nRB * Gc; }
 };
 
-// Choose how many 256 x 512 sub-tiles each workgroup sweeps so that about
-// `target` workgroups cover the pair.
-Plan make_plan(int nA, int nB, int target)
+// Workgroups of 128 rows by gch chunks of 256 columns; gch (a power of two,
+// at most 8, so a workgroup's columns stay inside one aligned 2048-column
+// window) is the largest that still yields about `target` workgroups.
+Plan make_plan(int nA, int nB, long long target)
 {
     Plan p;
-    p.nRB = (nA + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
-    p.nCC = (nB + CHUNK - 1) / CHUNK;
-    p.rbPer = 1;
-    p.ccPer = 1;
-    auto groups = [&](int rb, int cc) {
-        return (long long)((p.nRB + rb - 1) / rb) * ((p.nCC + cc - 1) / cc);
-    };
-    while (groups(p.rbPer, p.ccPer) > target) {
-        const bool can_c = p.ccPer < MAX_CC_PER_WG && p.ccPer < p.nCC;
-        const bool can_r = p.rbPer < MAX_RB_PER_WG && p.rbPer < p.nRB;
-        if (can_c && (p.ccPer <= p.rbPer || !can_r))
-            ++p.ccPer;
-        else if (can_r)
-            ++p.rbPer;
-        else
-            break;
-    }
-    p.Gr = (p.nRB + p.rbPer - 1) / p.rbPer;
-    p.Gc = (p.nCC + p.ccPer - 1) / p.ccPer;
+    p.nRB = (nA + BLOCK_ROWS - 1) / BLOCK_ROWS;
+    p.nBC = (nB + CHUNK - 1) / CHUNK;
+    p.gch = MAX_GCH;
+    auto groups = [&](int g) { return (p.nBC + g - 1) / g; };
+    while (p.gch > 1 && (long long)p.nRB * groups(p.gch) < target)
+        p.gch >>= 1;
+    p.Gc = groups(p.gch);
     p.acc = align256((size_t)nA * 8) + align256((size_t)nA * 4) + align256((size_t)nB * 8);
     return p;
 }
 
-void fill_job(Job &J, const Plan &p, const uint8_t *A, int nA, const uint8_t *B, int nB,
-              uint8_t *acc, int32_t *res, serac_match *out, int32_t *count)
+int round_up(int n, int m) { return (n + m - 1) / m * m; }
+
+// Bytes of one set prepared in the requested roles.
+size_t prep_bytes(int n, bool asA, bool asB)
+{
+    size_t b = 0;
+    if (asA) {
+        const size_t r = (size_t)round_up(n, BLOCK_ROWS);
+        b += align256(r * DIM) + align256(r * 4);
+    }
+    if (asB) {
+        const size_t r = (size_t)round_up(n, CHUNK);
+        b += align256(r * DIM) + align256(r * 4);
+    }
+    return b;
+}
+
+// Places the prepared buffers of one set at q (advancing q).
+PrepJob make_prep(const uint8_t *X, int n, bool asA, bool asB, uint8_t *&q)
+{
+    PrepJob Q{};
+    Q.X = X;
+    Q.n = n;
+    if (asA) {
+        Q.rowsA = round_up(n, BLOCK_ROWS);
+        Q.Af = q;
+        q += align256((size_t)Q.rowsA * DIM);
+        Q.RT = reinterpret_cast<int32_t *>(q);
+        q += align256((size_t)Q.rowsA * 4);
+    }
+    if (asB) {
+        Q.rowsB = round_up(n, CHUNK);
+        Q.Bp = q;
+        q += align256((size_t)Q.rowsB * DIM);
+        Q.P = reinterpret_cast<uint32_t *>(q);
+        q += align256((size_t)Q.rowsB * 4);
+    }
+    return Q;
+}
+
+int prep_blocks(const PrepJob &Q)
+{
+    return (std::max(Q.rowsA, Q.rowsB) * 8 + PREP_THREADS - 1) / PREP_THREADS;
+}
+
+void fill_job(Job &J, const Plan &p, const uint8_t *A, int nA, const PrepJob &QA,
+              const uint8_t *B, int nB, const PrepJob &QB, uint8_t *acc, int32_t *res,
+              serac_match *out, int32_t *count)
 {
     J.A = A;
     J.B = B;
+    J.Af = QA.Af;
+    J.RT = QA.RT;
+    J.Bp = QB.Bp;
+    J.P = QB.P;
     J.nA = nA;
     J.nB = nB;
     J.nRB = p.nRB;
-    J.nCC = p.nCC;
-    J.rbPer = p.rbPer;
-    J.ccPer = p.ccPer;
-    J.Gr = p.Gr;
+    J.nBC = p.nBC;
+    J.gch = p.gch;
     J.Gc = p.Gc;
     uint8_t *q = acc;
     J.rbest = reinterpret_cast<unsigned long long *>(q);
@@ -930,6 +1030,29 @@ Gate make_gate(const Device *d, const serac_params *p)
     G.max_distance = p->max_distance;
     G.cross_check = p->cross_check;
     return G;
+}
+
+// Preparation and tile sweep of one pair (nA, nB > 0) on `stream`; the
+// prepared sets go to `prep` (prep_bytes(nA, 1, 0) + prep_bytes(nB, 0, 1)).
+void launch_pair(Job &J, const Plan &p, const uint8_t *A, int nA, const uint8_t *B, int nB,
+                 uint8_t *prep, bool cols, hipStream_t stream)
+{
+    uint8_t *q = prep;
+    PrepPair Q;
+    Q.q[0] = make_prep(A, nA, true, false, q);
+    Q.q[1] = make_prep(B, nB, false, true, q);
+    J.Af = Q.q[0].Af;
+    J.RT = Q.q[0].RT;
+    J.Bp = Q.q[1].Bp;
+    J.P = Q.q[1].P;
+    const dim3 pg(std::max(prep_blocks(Q.q[0]), prep_blocks(Q.q[1])), 2);
+    serac_prep_pair<<<pg, PREP_THREADS, 0, stream>>>(Q);
+    const int slot = prof_begin(stream);
+    if (cols)
+        serac_tiles_one<true><<<p.units(), TILE_THREADS, 0, stream>>>(J);
+    else
+        serac_tiles_one<false><<<p.units(), TILE_THREADS, 0, stream>>>(J);
+    prof_end(stream, slot);
 }
 
 }  // namespace
@@ -973,21 +1096,20 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int
         serac_zero_counts<<<1, 64, 0, stream>>>(nullptr, out->count, 1);
         return hipGetLastError() == hipSuccess ? SERAC_OK : SERAC_ERR_HIP;
     }
-    const Plan p = make_plan(nA, nB, d->cus);
+    const Plan p = make_plan(nA, nB, 2LL * d->cus);
+    const size_t res_bytes = align256((size_t)nA * 4);
     Workspace *w = nullptr;
-    st = get_workspace(stream, p.acc, (size_t)nA * 4, &w);
+    st = get_workspace(stream, p.acc,
+                       res_bytes + prep_bytes(nA, true, false) + prep_bytes(nB, false, true), &w);
     if (st != SERAC_OK)
         return st;
     Job J;
-    fill_job(J, p, descA, nA, descB, nB, w->acc, reinterpret_cast<int32_t *>(w->aux),
-             out->matches, out->count);
+    const PrepJob none{};
+    fill_job(J, p, descA, nA, none, descB, nB, none, w->acc,
+             reinterpret_cast<int32_t *>(w->aux), out->matches, out->count);
+    launch_pair(J, p, descA, nA, descB, nB, w->aux + res_bytes, params->cross_check != 0,
+                stream);
     const Gate G = make_gate(d, params);
-    const int slot = prof_begin(stream);
-    if (params->cross_check)
-        serac_tiles_one<true><<<p.Gr * p.Gc, THREADS, 0, stream>>>(J);
-    else
-        serac_tiles_one<false><<<p.Gr * p.Gc, THREADS, 0, stream>>>(J);
-    prof_end(stream, slot);
     serac_gate_one<<<(nA + GATE_THREADS - 1) / GATE_THREADS, GATE_THREADS, 0, stream>>>(J, G);
     serac_compact_one<<<1, COMPACT_THREADS, 0, stream>>>(J);
     if (hipGetLastError() != hipSuccess) {
@@ -1028,39 +1150,66 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
     // pairs with an empty side only get a zero count
     std::vector<int32_t *> zero;
     std::vector<int> live;
+    std::vector<char> asA(num_images, 0), asB(num_images, 0);
     for (int q = 0; q < num_pairs; ++q) {
-        if (n[pairs[q].a] == 0 || n[pairs[q].b] == 0)
+        if (n[pairs[q].a] == 0 || n[pairs[q].b] == 0) {
             zero.push_back(out[q].count);
-        else
+        } else {
             live.push_back(q);
+            asA[pairs[q].a] = 1;
+            asB[pairs[q].b] = 1;
+        }
+    }
+    // every image is prepared once, in the roles its pairs use
+    std::vector<int> prepped;
+    size_t prep_total = 0;
+    for (int k = 0; k < num_images; ++k) {
+        if (asA[k] || asB[k]) {
+            prepped.push_back(k);
+            prep_total += prep_bytes(n[k], asA[k], asB[k]);
+        }
     }
     // workgroups per pair: enough to fill the device a few times over
     const int nlive = (int)live.size();
-    const int target = nlive ? std::max(1, (4 * d->cus + nlive - 1) / nlive) : 1;
+    const long long target = nlive ? std::max(1LL, (4LL * d->cus + nlive - 1) / nlive) : 1;
     std::vector<Plan> plans(nlive);
     size_t acc_bytes = 0, res_bytes = 0;
-    int wgPerJob = 1, gatePerJob = 1;
+    int unitsPerJob = 1, gatePerJob = 1;
     for (int k = 0; k < nlive; ++k) {
         const serac_pair pr = pairs[live[k]];
         plans[k] = make_plan(n[pr.a], n[pr.b], target);
         acc_bytes += plans[k].acc;
         res_bytes += align256((size_t)n[pr.a] * 4);
-        wgPerJob = std::max(wgPerJob, plans[k].Gr * plans[k].Gc);
+        unitsPerJob = std::max(unitsPerJob, plans[k].units());
         gatePerJob = std::max(gatePerJob, (n[pr.a] + GATE_THREADS - 1) / GATE_THREADS);
     }
     const size_t jobs_bytes = align256(sizeof(Job) * (size_t)std::max(nlive, 1));
-    std::vector<uint8_t> host(jobs_bytes + align256(sizeof(int32_t *) * zero.size() + 8));
+    const size_t prepjobs_bytes = align256(sizeof(PrepJob) * std::max<size_t>(prepped.size(), 1));
+    const size_t zero_bytes = align256(sizeof(int32_t *) * zero.size() + 8);
+    std::vector<uint8_t> host(jobs_bytes + prepjobs_bytes + zero_bytes);
     Workspace *w = nullptr;
-    st = get_workspace(stream, acc_bytes, host.size() + res_bytes, &w);
+    st = get_workspace(stream, acc_bytes, host.size() + res_bytes + prep_total, &w);
     if (st != SERAC_OK)
         return st;
     Job *jobs = reinterpret_cast<Job *>(host.data());
-    int32_t **zp = reinterpret_cast<int32_t **>(host.data() + jobs_bytes);
-    uint8_t *q = w->acc, *rq = w->aux + host.size();
+    PrepJob *pjobs = reinterpret_cast<PrepJob *>(host.data() + jobs_bytes);
+    int32_t **zp = reinterpret_cast<int32_t **>(host.data() + jobs_bytes + prepjobs_bytes);
+    uint8_t *rq = w->aux + host.size();
+    uint8_t *pq = rq + res_bytes;
+    std::vector<int> slot(num_images, -1);
+    int prepBlocks = 1;
+    for (size_t k = 0; k < prepped.size(); ++k) {
+        const int im = prepped[k];
+        pjobs[k] = make_prep(desc[im], n[im], asA[im], asB[im], pq);
+        slot[im] = (int)k;
+        prepBlocks = std::max(prepBlocks, prep_blocks(pjobs[k]));
+    }
+    uint8_t *q = w->acc;
     for (int k = 0; k < nlive; ++k) {
         const serac_pair pr = pairs[live[k]];
-        fill_job(jobs[k], plans[k], desc[pr.a], n[pr.a], desc[pr.b], n[pr.b], q,
-                 reinterpret_cast<int32_t *>(rq), out[live[k]].matches, out[live[k]].count);
+        fill_job(jobs[k], plans[k], desc[pr.a], n[pr.a], pjobs[slot[pr.a]], desc[pr.b], n[pr.b],
+                 pjobs[slot[pr.b]], q, reinterpret_cast<int32_t *>(rq), out[live[k]].matches,
+                 out[live[k]].count);
         q += plans[k].acc;
         rq += align256((size_t)n[pr.a] * 4);
     }
@@ -1068,18 +1217,24 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
         zp[k] = zero[k];
     hipError_t e = hipMemcpyAsync(w->aux, host.data(), host.size(), hipMemcpyHostToDevice, stream);
     const Job *djobs = reinterpret_cast<const Job *>(w->aux);
-    int32_t *const *dzero = reinterpret_cast<int32_t *const *>(w->aux + jobs_bytes);
+    const PrepJob *dpjobs = reinterpret_cast<const PrepJob *>(w->aux + jobs_bytes);
+    int32_t *const *dzero =
+        reinterpret_cast<int32_t *const *>(w->aux + jobs_bytes + prepjobs_bytes);
     if (e == hipSuccess && !zero.empty())
         serac_zero_counts<<<((int)zero.size() + 255) / 256, 256, 0, stream>>>(dzero, nullptr,
                                                                          (int)zero.size());
     if (e == hipSuccess && nlive) {
+        serac_prep_many<<<dim3(prepBlocks, (unsigned)prepped.size()), PREP_THREADS, 0, stream>>>(
+            dpjobs);
         const Gate G = make_gate(d, params);
-        const int slot = prof_begin(stream);
+        const int pslot = prof_begin(stream);
         if (params->cross_check)
-            serac_tiles_many<true><<<nlive * wgPerJob, THREADS, 0, stream>>>(djobs, wgPerJob);
+            serac_tiles_many<true><<<nlive * unitsPerJob, TILE_THREADS, 0, stream>>>(djobs,
+                                                                                  unitsPerJob);
         else
-            serac_tiles_many<false><<<nlive * wgPerJob, THREADS, 0, stream>>>(djobs, wgPerJob);
-        prof_end(stream, slot);
+            serac_tiles_many<false><<<nlive * unitsPerJob, TILE_THREADS, 0, stream>>>(
+                djobs, unitsPerJob);
+        prof_end(stream, pslot);
         serac_gate_many<<<nlive * gatePerJob, GATE_THREADS, 0, stream>>>(djobs, gatePerJob, G);
         serac_compact_many<<<nlive, COMPACT_THREADS, 0, stream>>>(djobs);
     }
@@ -1109,17 +1264,21 @@ int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int3
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     if (nA == 0 && nB == 0)
         return SERAC_OK;
-    const Plan p = make_plan(std::max(nA, 1), std::max(nB, 1), d->cus);
+    const Plan p = make_plan(std::max(nA, 1), std::max(nB, 1), 2LL * d->cus);
     Workspace *w = nullptr;
-    st = get_workspace(stream, p.acc, 0, &w);
+    st = get_workspace(stream, p.acc,
+                       prep_bytes(std::max(nA, 1), true, false) +
+                           prep_bytes(std::max(nB, 1), false, true),
+                       &w);
     if (st != SERAC_OK)
         return st;
     Job J;
-    fill_job(J, p, descA, nA, descB, nB, w->acc, nullptr, nullptr, nullptr);
+    const PrepJob none{};
+    fill_job(J, p, descA, nA, none, descB, nB, none, w->acc, nullptr, nullptr, nullptr);
     // with an empty side nothing is raised: rows report (0, -1, 0) and
     // columns (0, -1) from the cleared accumulators
     if (nA > 0 && nB > 0)
-        serac_tiles_one<true><<<p.Gr * p.Gc, THREADS, 0, stream>>>(J);
+        launch_pair(J, p, descA, nA, descB, nB, w->aux, true, stream);
     if (nA > 0)
         serac_export_rows<<<(nA + 255) / 256, 256, 0, stream>>>(J, row_top2);
     if (nB > 0)

@@ -53,9 +53,17 @@ def check_pair(serac, A, B, max_ratio=0.8, max_distance=math.inf, cross_check=Tr
     if top2:
         row, col = serac.top2(a, b)
         orow, ocol = oracle.top2(A, B)
-        assert np.array_equal(row.cpu().numpy(), orow), label + " row_top2"
-        assert np.array_equal(col.cpu().numpy(), ocol), label + " col_best"
+        assert_rows_equal(row.cpu().numpy(), orow, label + " row_top2")
+        assert_rows_equal(col.cpu().numpy(), ocol, label + " col_best")
     return got
+
+
+def assert_rows_equal(got, want, label):
+    """Exact equality with the first differing rows named on failure."""
+    assert got.shape == want.shape, (label, got.shape, want.shape)
+    bad = np.flatnonzero((got != want).any(axis=1))
+    assert bad.size == 0, (f"{label}: {bad.size} rows differ, first "
+                           f"{[(int(i), got[i].tolist(), want[i].tolist()) for i in bad[:6]]}")
 
 
 SMALL = [(1, 1), (1, 2), (2, 1), (3, 17), (17, 3), (40, 40), (255, 511), (256, 512),
