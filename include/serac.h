@@ -138,14 +138,16 @@ int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB,
                     int32_t *col_best);
 
 /*
- * Profiling of the fused tile kernel (the kernel that does the contraction
- * and the on-the-fly reductions).  serac_profile_start arms up to
- * max_launches pairs of HIP events; every following launch of that kernel
- * by serac_match_pair or serac_match_pairs records one event before and one
- * after it on the call's stream.  serac_profile_stop waits for the recorded
- * events, returns the summed device time in milliseconds and the number of
- * launches timed, and disarms.  Not thread-safe against concurrent matching
- * calls from other threads; meant for benchmarks.
+ * Timing of the fused tile kernel (the kernel that does the contraction and
+ * the on-the-fly reductions), for benchmarks.  serac_profile_start arms up
+ * to max_launches pairs of HIP events; each following launch of that kernel
+ * by serac_match_pair, serac_match_pairs or serac_top2_pair is dispatched
+ * with hipExtLaunchKernel carrying one pair as its start and stop events
+ * (recorded by the dispatch itself on the call's stream, so the launches
+ * stay back to back).  serac_profile_stop waits for the recorded events,
+ * returns the summed device time in milliseconds and the number of launches
+ * timed, and disarms.  Not thread-safe against concurrent matching calls
+ * from other threads.
  * Errors: SERAC_ERR_INVALID_ARG (max_launches outside [1, 1048576], NULL
  * outputs, stop without start), SERAC_ERR_HIP.
  */

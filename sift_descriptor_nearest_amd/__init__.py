@@ -70,11 +70,10 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.serac_top2_pair.argtypes = [vp, i32, vp, i32, vp, vp, vp]
     L.serac_profile_start.argtypes = [i32]
     L.serac_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
-    L.serac_profile_start.restype = ctypes.c_int
-    L.serac_profile_stop.restype = ctypes.c_int
     L.serac_status_string.argtypes = [ctypes.c_int]
     L.serac_status_string.restype = ctypes.c_char_p
-    for f in (L.serac_match_pair, L.serac_match_pairs, L.serac_top2_pair):
+    for f in (L.serac_match_pair, L.serac_match_pairs, L.serac_top2_pair,
+              L.serac_profile_start, L.serac_profile_stop):
         f.restype = ctypes.c_int
     _lib = L
     return L
@@ -182,7 +181,8 @@ def top2(a, b):
 
 
 def profile_start(max_launches: int) -> None:
-    """Arm HIP-event timing of the next max_launches tile-kernel launches."""
+    """Time the next max_launches tile-kernel launches with HIP events
+    attached to their dispatches."""
     rc = library().serac_profile_start(int(max_launches))
     if rc != SERAC_OK:
         raise SeracError(rc, "serac_profile_start")

@@ -23,7 +23,8 @@
 //     row terms, B as 256-column chunks of eight 16-byte "planes" plus each
 //     column's key addend.  The tile kernel then streams B chunks straight
 //     from global memory into LDS (global_load_lds_dwordx4: no registers,
-//     no vector instructions) two chunks ahead of use.
+//     no vector instructions), fetching chunk c+1 into the second buffer
+//     while chunk c is swept.
 //   * A workgroup is four waves, one per SIMD, 128 rows of A by up to 2048
 //     columns of B; two workgroups share a CU.  Each wave keeps the operand
 //     fragments of its 32 rows in registers and sweeps 32-column tiles two at
@@ -55,6 +56,7 @@
 //     one a CPU makes; the ratio test is one IEEE multiply and compare.
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cmath>
 #include <cstdint>
@@ -122,8 +124,8 @@ struct Job {
     int32_t nA, nB;
     int32_t nRB, nBC;        // 128-row blocks of A, 256-column chunks of B
     int32_t gch, Gc;         // chunks per workgroup (1, 2, 4 or 8), column groups
-    unsigned long long *rbest;  // [nA] (best << 32) | ~column   (max: lowest column)
-    uint32_t *rsec;             // [nA] second-best score
+    unsigned long long *rslot;  // [Gc][nA] one row result per column group (see pack_slot)
+    uint32_t *rs1;              // [nA] best score per row (column export scratch)
     unsigned long long *cbest;  // [nB] (best << 32) | ~slice    (max: lowest slice)
     int32_t *res;            // [nA] accepted column of each row, or -1 (scratch)
     serac_match *out;        // [>= nA]
@@ -136,6 +138,24 @@ struct Gate {
     double max_distance;
     int32_t cross_check;
 };
+
+// A row's result over one column group packed into 64 bits, ordered like
+// the key (score first, then lowest column):
+//   bits 63..41  best score S1 (< 2^23)
+//   bits 40..23  2^18 - 1 - column of S1 (columns < 2^18)
+//   bits 22..0   second score S2 (< 2^23)
+// A group whose best score is 0 stores 0.
+constexpr int SLOT_COL_BITS = 18;
+constexpr uint32_t SLOT_COL_MAX = (1u << SLOT_COL_BITS) - 1;
+
+__host__ __device__ __forceinline__ unsigned long long pack_slot(uint32_t S1, uint32_t col,
+                                                                 uint32_t S2)
+{
+    if (S1 == 0u)
+        return 0ull;
+    return ((unsigned long long)S1 << 41) |
+           ((unsigned long long)(SLOT_COL_MAX - col) << 23) | (unsigned long long)S2;
+}
 
 __device__ __forceinline__ uint32_t umax3(uint32_t a, uint32_t b, uint32_t c)
 {
@@ -243,9 +263,13 @@ __global__ __launch_bounds__(PREP_THREADS) void serac_prep_many(const PrepJob *_
 //
 // Schedule per chunk (4 tile pairs, k = 0..3): step k issues the MFMAs of
 // pair k, runs the epilogue of pair k-1 (pair 3 of the previous chunk for
-// k = 0) and reads the operands of pair k+1 from LDS; the accumulators and
-// operands alternate between two register sets.  Chunk c+2 is fetched into
-// LDS while chunks c and c+1 are in use.
+// k = 0) and reads the operands of pair k+1 from LDS; the accumulators
+// alternate between two register sets.  Chunk c+1 is fetched into the other
+// LDS buffer while chunk c is swept.
+//
+// Each workgroup writes, per row and column group, one packed slot (best,
+// column, second) with a plain store, and raises the column best of its
+// columns with 64-bit atomic maxima; nothing is read back.
 template <bool COLS>
 __device__ __forceinline__ void tiles_body(const Job &J, int u)
 {
@@ -290,17 +314,14 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
             load_lds16(J.P + (size_t)(c0 + c) * CHUNK + lane * 4, sP + buf * CHUNK);
     };
     stage(0, 0);
-    if (nch > 1)
-        stage(1, 1);
     if (COLS) {
         for (int k = tid; k < nch * CHUNK; k += TILE_THREADS)
             sCol[k] = 0u;
     }
-    if (nch > 1)
-        wait_vmcnt<8>();                     // chunk 0 (and the A loads) landed
-    else
-        wait_vmcnt<0>();
+    wait_vmcnt<0>();                         // chunk 0 and the A operands landed
     __syncthreads();
+    if (nch > 1)
+        stage(1, 1);                         // needed one chunk from now
 
     v4i bf[2][4];        // [tile][k-slice]: operands of the next pair
     uint32_t pk[2][2];   // [set][tile] key addends
@@ -452,20 +473,14 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
         K1 = max(K1, o1);
         K2 = umax3(lo, K2, o2);
     }
-    // publish this row block's top-2 over the workgroup's columns: the
-    // atomic max keeps the best key over all workgroups; whichever key
-    // loses an exchange (or this group's own second) raises the row's
-    // second score, so the second ends as the runner-up of all
-    // candidates, ties counted.
-    const uint32_t S1 = K1 >> 9, S2 = K2 >> 9;
+    // publish this row block's top-2 over the workgroup's columns as one
+    // packed slot per (row, column group); the gate merges the groups
     const int row = rb * BLOCK_ROWS + w * WAVE_ROWS + n;
-    if (h == 0 && row < J.nA && S1 > 0u) {
+    if (h == 0 && row < J.nA) {
+        const uint32_t S1 = K1 >> 9, S2 = K2 >> 9;
         const int window = (c0 * CHUNK) & ~(GROUP_MAX - 1);
         const uint32_t col = (uint32_t)(window + 32 * (511 - (int)(K1 & 511u)) + L1);
-        const unsigned long long key = ((unsigned long long)S1 << 32) | (0xFFFFFFFFu - col);
-        const unsigned long long old = atomicMax(J.rbest + row, key);
-        const uint32_t loser = (uint32_t)(min(old, key) >> 32);
-        atomicMax(J.rsec + row, max(loser, S2));
+        J.rslot[(size_t)cg * J.nA + row] = pack_slot(S1, col, S2);
     }
 
     if (COLS) {
@@ -518,18 +533,104 @@ __device__ int32_t dot_exact(const uint8_t *a, const uint8_t *b)
     return (int32_t)s;
 }
 
-// Row i's published result: best score, its column (-1 below the zero
-// floor) and the second score.
-__device__ __forceinline__ void row_result(const Job &J, unsigned long long key, uint32_t sec,
-                                           uint32_t &S1, int32_t &I1, uint32_t &S2)
+// Row i's result over all column groups: best score, its column (-1 below
+// the zero floor) and the second score.  The best slot wins (highest score,
+// then lowest column); the second is the largest of every group's second
+// and every other group's best, ties counted.
+__device__ __forceinline__ void row_result(const Job &J, int i, uint32_t &S1, int32_t &I1,
+                                           uint32_t &S2)
 {
-    S1 = (uint32_t)(key >> 32);
-    I1 = S1 ? (int32_t)(0xFFFFFFFFu - (uint32_t)key) : -1;
-    S2 = sec;
+    unsigned long long best = 0ull;
+    uint32_t sec = 0u, loser = 0u;
+    const int groups = J.nB > 0 ? J.Gc : 0;   // no sweep ran against an empty set
+    for (int g0 = 0; g0 < groups; g0 += 8) {
+        // eight groups' slots in flight at once
+        unsigned long long v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            v[k] = g0 + k < groups ? J.rslot[(size_t)(g0 + k) * J.nA + i] : 0ull;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const unsigned long long lo = min(best, v[k]);
+            loser = max(loser, (uint32_t)(lo >> 41));
+            best = max(best, v[k]);
+            sec = max(sec, (uint32_t)(v[k] & 0x7FFFFFu));
+        }
+    }
+    S1 = (uint32_t)(best >> 41);
+    I1 = S1 ? (int32_t)(SLOT_COL_MAX - (uint32_t)((best >> 23) & SLOT_COL_MAX)) : -1;
+    S2 = max(sec, loser);
+}
+
+// Ordered compaction of one pair's decisions res[0, nA) into out by one
+// workgroup of GATE_THREADS: rows are taken 32 per thread (8192 per pass), and
+// a workgroup-wide exclusive scan of the per-thread counts places each
+// thread's matches.  Also clears the pair's column accumulators and sets the
+// count.
+__device__ __forceinline__ void compact_pair(const Job &J)
+{
+    constexpr int PER = 32;
+    constexpr int WAVES = GATE_THREADS / 64;
+    __shared__ int32_t sWave[WAVES];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int32_t run = 0;
+    for (int base = 0; base < J.nA; base += PER * GATE_THREADS) {
+        const int i0 = base + PER * tid;
+        int32_t v[PER];
+        if (i0 + PER <= J.nA) {
+#pragma unroll
+            for (int q = 0; q < PER / 4; ++q) {
+                const int4 x = *reinterpret_cast<const int4 *>(J.res + i0 + 4 * q);
+                v[4 * q] = x.x;
+                v[4 * q + 1] = x.y;
+                v[4 * q + 2] = x.z;
+                v[4 * q + 3] = x.w;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < PER; ++k)
+                v[k] = (i0 + k < J.nA) ? J.res[i0 + k] : -1;
+        }
+        int32_t cnt = 0;
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+            cnt += v[k] >= 0;
+        int32_t inc = cnt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int32_t t = __shfl_up(inc, d);
+            if (lane >= d)
+                inc += t;
+        }
+        if (lane == 63)
+            sWave[wv] = inc;
+        __syncthreads();
+        int32_t before = 0, total = 0;
+#pragma unroll
+        for (int k = 0; k < WAVES; ++k) {
+            before += (k < wv) ? sWave[k] : 0;
+            total += sWave[k];
+        }
+        int32_t o = run + before + inc - cnt;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            if (v[k] >= 0) {
+                J.out[o].a = (uint32_t)(i0 + k);
+                J.out[o].b = (uint32_t)v[k];
+                ++o;
+            }
+        }
+        run += total;
+        __syncthreads();                     // sWave reused by the next pass
+    }
+    for (int j = tid; j < J.nB; j += GATE_THREADS)
+        J.cbest[j] = 0ull;
+    if (tid == 0)
+        *J.count = run;
 }
 
 // Gates and cross-check of 256 rows: res[i] = the accepted column of row i,
-// or -1.  The row accumulators are cleared as they are consumed.
+// or -1.
 __device__ __forceinline__ void gate_body(const Job &J, int wg, const Gate &G)
 {
     __shared__ uint32_t sS1[GATE_THREADS];
@@ -537,11 +638,8 @@ __device__ __forceinline__ void gate_body(const Job &J, int wg, const Gate &G)
     const int i = wg * GATE_THREADS + tid;
     uint32_t S1 = 0u, S2 = 0u;
     int32_t I1 = -1;
-    if (i < J.nA) {
-        row_result(J, J.rbest[i], J.rsec[i], S1, I1, S2);
-        J.rbest[i] = 0ull;
-        J.rsec[i] = 0u;
-    }
+    if (i < J.nA)
+        row_result(J, i, S1, I1, S2);
     sS1[tid] = S1;
     const bool cand = I1 >= 0 && I1 < J.nB;
     double d1 = 0.0, d2 = 0.0;
@@ -591,10 +689,13 @@ __global__ __launch_bounds__(GATE_THREADS) void serac_gate_many(const Job *__res
     gate_body(J, wg, G);
 }
 
-// Ordered compaction of one pair by one workgroup: rows are taken 8192 at a
-// time, eight consecutive rows per thread, and a workgroup-wide exclusive
-// scan of the per-thread counts places each thread's matches.  The column
-// accumulators, read by every gate group, are cleared here.
+// Ordered compaction of one pair by one workgroup, after all its gate
+// groups: rows are taken 8192 at a time, eight consecutive rows per thread,
+// and a workgroup-wide exclusive scan of the per-thread counts places each
+// thread's matches.  The column accumulators, read by every gate group, are
+// cleared here.  (A single kernel that lets the last gate group compact
+// behind a fence and ticket was measured slower on gfx950: each
+// device-scope fence writes back the XCD's whole L2.)
 __device__ __forceinline__ void compact_body(const Job &J)
 {
     __shared__ int32_t sWave[COMPACT_THREADS / 64];
@@ -682,7 +783,7 @@ __global__ void serac_clear(uint4 *p, size_t n)
 }
 
 // Export of the row reduction: row_top2[i] = (best, idx, second).  The best
-// score is kept in rsec for the column export, rbest is cleared.
+// score is kept in rs1 for the column export.
 __global__ void serac_export_rows(Job J, int32_t *row_top2)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -690,12 +791,11 @@ __global__ void serac_export_rows(Job J, int32_t *row_top2)
         return;
     uint32_t S1, S2;
     int32_t I1;
-    row_result(J, J.rbest[i], J.rsec[i], S1, I1, S2);
+    row_result(J, i, S1, I1, S2);
     row_top2[3 * (size_t)i] = (int32_t)S1;
     row_top2[3 * (size_t)i + 1] = I1;
     row_top2[3 * (size_t)i + 2] = (int32_t)S2;
-    J.rbest[i] = 0ull;
-    J.rsec[i] = S1;
+    J.rs1[i] = S1;
 }
 
 // Export of the column reduction: col_best[j] = (best, lowest row).  The
@@ -714,7 +814,7 @@ __global__ void serac_export_cols(Job J, int32_t *col_best)
     if (C1 > 0u) {
         const uint8_t *b = J.B + (size_t)j * DIM;
         for (int i = slice * SLICE; i < min(slice * SLICE + SLICE, J.nA); ++i) {
-            if (J.rsec[i] >= C1 && (uint32_t)dot_exact(J.A + (size_t)i * DIM, b) == C1) {
+            if (J.rs1[i] >= C1 && (uint32_t)dot_exact(J.A + (size_t)i * DIM, b) == C1) {
                 idx = i;
                 break;
             }
@@ -725,13 +825,6 @@ __global__ void serac_export_cols(Job J, int32_t *col_best)
     J.cbest[j] = 0ull;
 }
 
-// Clears rsec after the column export has used it.
-__global__ void serac_export_clear(Job J)
-{
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < J.nA)
-        J.rsec[i] = 0u;
-}
 
 // ------------------------------------------------------------------ host
 
@@ -745,31 +838,27 @@ struct Device {
 std::mutex g_mutex;
 Device g_devices[64];
 
-// Event pairs around tile-kernel launches while profiling is armed.
+// Dispatch-attached timing of tile-kernel launches while profiling is armed:
+// each launch carries its own start and stop events (hipExtLaunchKernel), so
+// the queue gets no extra marker packets and the launches stay back to back.
 struct Profile {
     bool armed = false;
     int used = 0;
-    std::vector<hipEvent_t> ev;   // [2 * max]: begin, end
+    std::vector<hipEvent_t> ev;   // [2 * max]: start, stop
 };
 std::mutex g_prof_mutex;
 Profile g_prof;
 
-int prof_begin(hipStream_t s)
+// Event pair for the next tile launch, or nulls when not armed / full.
+void prof_slot(hipEvent_t &start, hipEvent_t &stop)
 {
+    start = stop = nullptr;
     std::lock_guard<std::mutex> lock(g_prof_mutex);
     if (!g_prof.armed || 2 * (g_prof.used + 1) > (int)g_prof.ev.size())
-        return -1;
-    const int slot = g_prof.used++;
-    (void)hipEventRecord(g_prof.ev[2 * slot], s);
-    return slot;
-}
-
-void prof_end(hipStream_t s, int slot)
-{
-    if (slot < 0)
         return;
-    std::lock_guard<std::mutex> lock(g_prof_mutex);
-    (void)hipEventRecord(g_prof.ev[2 * slot + 1], s);
+    start = g_prof.ev[2 * g_prof.used];
+    stop = g_prof.ev[2 * g_prof.used + 1];
+    ++g_prof.used;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -911,7 +1000,8 @@ void mark_dirty(Workspace *w)
 
 struct Plan {
     int nRB, nBC, gch, Gc;
-    size_t acc;   // bytes of accumulators
+    size_t acc;       // bytes of accumulators (zero between calls): cbest
+    size_t scratch;   // bytes of per-call scratch: res / rs1, then rslot
     int units() const { return nRB * Gc; }
 };
 
@@ -928,7 +1018,8 @@ Plan make_plan(int nA, int nB, long long target)
     while (p.gch > 1 && (long long)p.nRB * groups(p.gch) < target)
         p.gch >>= 1;
     p.Gc = groups(p.gch);
-    p.acc = align256((size_t)nA * 8) + align256((size_t)nA * 4) + align256((size_t)nB * 8);
+    p.acc = align256((size_t)nB * 8);
+    p.scratch = align256((size_t)nA * 4) + align256((size_t)p.Gc * nA * 8);
     return p;
 }
 
@@ -978,7 +1069,7 @@ int prep_blocks(const PrepJob &Q)
 }
 
 void fill_job(Job &J, const Plan &p, const uint8_t *A, int nA, const PrepJob &QA,
-              const uint8_t *B, int nB, const PrepJob &QB, uint8_t *acc, int32_t *res,
+              const uint8_t *B, int nB, const PrepJob &QB, uint8_t *acc, uint8_t *scratch,
               serac_match *out, int32_t *count)
 {
     J.A = A;
@@ -993,13 +1084,11 @@ void fill_job(Job &J, const Plan &p, const uint8_t *A, int nA, const PrepJob &QA
     J.nBC = p.nBC;
     J.gch = p.gch;
     J.Gc = p.Gc;
-    uint8_t *q = acc;
-    J.rbest = reinterpret_cast<unsigned long long *>(q);
-    q += align256((size_t)nA * 8);
-    J.rsec = reinterpret_cast<uint32_t *>(q);
-    q += align256((size_t)nA * 4);
-    J.cbest = reinterpret_cast<unsigned long long *>(q);
-    J.res = res;
+    J.cbest = reinterpret_cast<unsigned long long *>(acc);
+    // res (matching) and rs1 (export) are never needed in the same call
+    J.res = reinterpret_cast<int32_t *>(scratch);
+    J.rs1 = reinterpret_cast<uint32_t *>(scratch);
+    J.rslot = reinterpret_cast<unsigned long long *>(scratch + align256((size_t)nA * 4));
     J.out = out;
     J.count = count;
 }
@@ -1032,6 +1121,24 @@ Gate make_gate(const Device *d, const serac_params *p)
     return G;
 }
 
+void launch_tiles(const Job &J, const Plan &p, bool cols, hipStream_t stream)
+{
+    hipEvent_t e0, e1;
+    prof_slot(e0, e1);
+    if (e0) {
+        if (cols)
+            hipExtLaunchKernelGGL(serac_tiles_one<true>, dim3(p.units()), dim3(TILE_THREADS), 0,
+                                  stream, e0, e1, 0, J);
+        else
+            hipExtLaunchKernelGGL(serac_tiles_one<false>, dim3(p.units()), dim3(TILE_THREADS), 0,
+                                  stream, e0, e1, 0, J);
+    } else if (cols) {
+        serac_tiles_one<true><<<p.units(), TILE_THREADS, 0, stream>>>(J);
+    } else {
+        serac_tiles_one<false><<<p.units(), TILE_THREADS, 0, stream>>>(J);
+    }
+}
+
 // Preparation and tile sweep of one pair (nA, nB > 0) on `stream`; the
 // prepared sets go to `prep` (prep_bytes(nA, 1, 0) + prep_bytes(nB, 0, 1)).
 void launch_pair(Job &J, const Plan &p, const uint8_t *A, int nA, const uint8_t *B, int nB,
@@ -1047,12 +1154,7 @@ void launch_pair(Job &J, const Plan &p, const uint8_t *A, int nA, const uint8_t 
     J.P = Q.q[1].P;
     const dim3 pg(std::max(prep_blocks(Q.q[0]), prep_blocks(Q.q[1])), 2);
     serac_prep_pair<<<pg, PREP_THREADS, 0, stream>>>(Q);
-    const int slot = prof_begin(stream);
-    if (cols)
-        serac_tiles_one<true><<<p.units(), TILE_THREADS, 0, stream>>>(J);
-    else
-        serac_tiles_one<false><<<p.units(), TILE_THREADS, 0, stream>>>(J);
-    prof_end(stream, slot);
+    launch_tiles(J, p, cols, stream);
 }
 
 }  // namespace
@@ -1097,17 +1199,15 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int
         return hipGetLastError() == hipSuccess ? SERAC_OK : SERAC_ERR_HIP;
     }
     const Plan p = make_plan(nA, nB, 2LL * d->cus);
-    const size_t res_bytes = align256((size_t)nA * 4);
     Workspace *w = nullptr;
     st = get_workspace(stream, p.acc,
-                       res_bytes + prep_bytes(nA, true, false) + prep_bytes(nB, false, true), &w);
+                       p.scratch + prep_bytes(nA, true, false) + prep_bytes(nB, false, true), &w);
     if (st != SERAC_OK)
         return st;
     Job J;
     const PrepJob none{};
-    fill_job(J, p, descA, nA, none, descB, nB, none, w->acc,
-             reinterpret_cast<int32_t *>(w->aux), out->matches, out->count);
-    launch_pair(J, p, descA, nA, descB, nB, w->aux + res_bytes, params->cross_check != 0,
+    fill_job(J, p, descA, nA, none, descB, nB, none, w->acc, w->aux, out->matches, out->count);
+    launch_pair(J, p, descA, nA, descB, nB, w->aux + p.scratch, params->cross_check != 0,
                 stream);
     const Gate G = make_gate(d, params);
     serac_gate_one<<<(nA + GATE_THREADS - 1) / GATE_THREADS, GATE_THREADS, 0, stream>>>(J, G);
@@ -1179,7 +1279,7 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
         const serac_pair pr = pairs[live[k]];
         plans[k] = make_plan(n[pr.a], n[pr.b], target);
         acc_bytes += plans[k].acc;
-        res_bytes += align256((size_t)n[pr.a] * 4);
+        res_bytes += plans[k].scratch;
         unitsPerJob = std::max(unitsPerJob, plans[k].units());
         gatePerJob = std::max(gatePerJob, (n[pr.a] + GATE_THREADS - 1) / GATE_THREADS);
     }
@@ -1208,10 +1308,9 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
     for (int k = 0; k < nlive; ++k) {
         const serac_pair pr = pairs[live[k]];
         fill_job(jobs[k], plans[k], desc[pr.a], n[pr.a], pjobs[slot[pr.a]], desc[pr.b], n[pr.b],
-                 pjobs[slot[pr.b]], q, reinterpret_cast<int32_t *>(rq), out[live[k]].matches,
-                 out[live[k]].count);
+                 pjobs[slot[pr.b]], q, rq, out[live[k]].matches, out[live[k]].count);
         q += plans[k].acc;
-        rq += align256((size_t)n[pr.a] * 4);
+        rq += plans[k].scratch;
     }
     for (size_t k = 0; k < zero.size(); ++k)
         zp[k] = zero[k];
@@ -1227,14 +1326,15 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
         serac_prep_many<<<dim3(prepBlocks, (unsigned)prepped.size()), PREP_THREADS, 0, stream>>>(
             dpjobs);
         const Gate G = make_gate(d, params);
-        const int pslot = prof_begin(stream);
+        hipEvent_t e0, e1;
+        prof_slot(e0, e1);
+        const dim3 grid(nlive * unitsPerJob);
         if (params->cross_check)
-            serac_tiles_many<true><<<nlive * unitsPerJob, TILE_THREADS, 0, stream>>>(djobs,
-                                                                                  unitsPerJob);
+            hipExtLaunchKernelGGL(serac_tiles_many<true>, grid, dim3(TILE_THREADS), 0, stream,
+                                  e0, e1, 0, djobs, unitsPerJob);
         else
-            serac_tiles_many<false><<<nlive * unitsPerJob, TILE_THREADS, 0, stream>>>(
-                djobs, unitsPerJob);
-        prof_end(stream, pslot);
+            hipExtLaunchKernelGGL(serac_tiles_many<false>, grid, dim3(TILE_THREADS), 0, stream,
+                                  e0, e1, 0, djobs, unitsPerJob);
         serac_gate_many<<<nlive * gatePerJob, GATE_THREADS, 0, stream>>>(djobs, gatePerJob, G);
         serac_compact_many<<<nlive, COMPACT_THREADS, 0, stream>>>(djobs);
     }
@@ -1267,24 +1367,22 @@ int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int3
     const Plan p = make_plan(std::max(nA, 1), std::max(nB, 1), 2LL * d->cus);
     Workspace *w = nullptr;
     st = get_workspace(stream, p.acc,
-                       prep_bytes(std::max(nA, 1), true, false) +
+                       p.scratch + prep_bytes(std::max(nA, 1), true, false) +
                            prep_bytes(std::max(nB, 1), false, true),
                        &w);
     if (st != SERAC_OK)
         return st;
     Job J;
     const PrepJob none{};
-    fill_job(J, p, descA, nA, none, descB, nB, none, w->acc, nullptr, nullptr, nullptr);
+    fill_job(J, p, descA, nA, none, descB, nB, none, w->acc, w->aux, nullptr, nullptr);
     // with an empty side nothing is raised: rows report (0, -1, 0) and
     // columns (0, -1) from the cleared accumulators
     if (nA > 0 && nB > 0)
-        launch_pair(J, p, descA, nA, descB, nB, w->aux, true, stream);
+        launch_pair(J, p, descA, nA, descB, nB, w->aux + p.scratch, true, stream);
     if (nA > 0)
         serac_export_rows<<<(nA + 255) / 256, 256, 0, stream>>>(J, row_top2);
     if (nB > 0)
         serac_export_cols<<<(nB + 255) / 256, 256, 0, stream>>>(J, col_best);
-    if (nA > 0)
-        serac_export_clear<<<(nA + 255) / 256, 256, 0, stream>>>(J);
     if (hipGetLastError() != hipSuccess) {
         mark_dirty(w);
         return SERAC_ERR_HIP;
@@ -1298,11 +1396,11 @@ int serac_profile_start(int32_t max_launches)
         return SERAC_ERR_INVALID_ARG;
     std::lock_guard<std::mutex> lock(g_prof_mutex);
     for (hipEvent_t e : g_prof.ev)
-        (void)hipEventDestroy(e);
-    g_prof.ev.clear();
+        if (e)
+            (void)hipEventDestroy(e);
+    g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
     g_prof.used = 0;
     g_prof.armed = false;
-    g_prof.ev.resize(2 * (size_t)max_launches);
     for (auto &e : g_prof.ev) {
         if (hipEventCreate(&e) != hipSuccess) {
             e = nullptr;

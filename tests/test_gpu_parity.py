@@ -194,3 +194,13 @@ def test_batch_48x8192(serac):
         if (ia, ib) in bt.truth:
             t = {tuple(x) for x in bt.truth[(ia, ib)].tolist()}
             assert t <= {tuple(x) for x in want.astype(np.int64).tolist()}
+
+
+def test_profiled_launches_exact(serac):
+    """Tile launches timed with dispatch-attached events give the same
+    results, and the timing is returned for each of them."""
+    p = synth.workload("pair_1000x1200")
+    serac.profile_start(8)
+    check_pair(serac, p.A, p.B, **p.params(), label="profiled")
+    ms, n = serac.profile_stop()
+    assert n == 2 and 0.0 < ms < 1000.0      # one match_pair and one top2 launch
