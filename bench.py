@@ -8,14 +8,14 @@ Inputs are resident in HBM before the timed region; outputs are
 preallocated, poisoned before the warm-up, and the last step's match list
 is compared byte for byte with the CPU oracle after the timed region.
 
-Prints one JSON line.  `value` and `ms_per_step` come from the timed region
-alone (no events in it).  `roofline` is for the dominant kernel (the fused
-tile kernel): its average launch duration over up to 500 further identical
-steps, from HIP start/stop events attached to each of its dispatches on the
-launch stream (hipExtLaunchKernel).  Those events make the host enqueue more
-slowly, which is why they stay out of the timed region; under rocprofv3
-their readings are not meaningful (the profiler takes over the dispatch
-timestamps), so the profiler's own kernel trace is the comparison.
+Prints one JSON line.  `value` and `ms_per_step` come from the timed region.
+`roofline` is for the dominant kernel (the fused tile kernel): its average
+launch duration over the timed region, from HIP start/stop events attached
+to one of every PROFILE_EVERY of its dispatches on the launch stream
+(hipExtLaunchKernel; events on every dispatch would slow the enqueueing
+host enough to leave the queue idle between steps).  Under rocprofv3 these
+readings are not meaningful (the profiler takes over the dispatch
+timestamps), so there the profiler's own kernel trace is the measurement.
 `cpu_baseline` is the oracle on this host's cores, timed on a bounded
 number of full-pair runs.
 """
@@ -34,6 +34,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, published
+PROFILE_EVERY = 8            # tile-kernel launches per event-timed one
 TRAFFIC = os.path.join(ROOT, "profiles", "traffic_tiles_pair_8192x8192.json")
 KERNEL_SRC = os.path.join(ROOT, "sift_descriptor_nearest_amd", "csrc", "serac.hip")
 
@@ -124,23 +125,17 @@ def main() -> int:
         serac.match_pair_into(a, b, out, cnt, **prm)
     torch.cuda.synchronize()
 
+    # the dominant kernel's launch duration, live in the timed region: HIP
+    # events attached to one tile-kernel dispatch in PROFILE_EVERY
+    serac.profile_start(args.steps // PROFILE_EVERY + 1, PROFILE_EVERY)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         serac.match_pair_into(a, b, out, cnt, **prm)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    got = out[: int(cnt.item())].cpu().numpy().astype(np.uint32)
-
-    # the dominant kernel's launch duration: the same steps again with HIP
-    # events attached to every tile-kernel dispatch (the event handling slows
-    # the host's enqueueing, so these steps are not the timed ones)
-    launches_req = max(1, min(args.steps, 500))
-    serac.profile_start(launches_req)
-    for _ in range(launches_req):
-        serac.match_pair_into(a, b, out, cnt, **prm)
-    torch.cuda.synchronize()
     kms, launches = serac.profile_stop()
+    got = out[: int(cnt.item())].cpu().numpy().astype(np.uint32)
 
     ops = 2.0 * 128 * nA * nB
     wall = t1 - t0

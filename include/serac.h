@@ -140,18 +140,20 @@ int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB,
 /*
  * Timing of the fused tile kernel (the kernel that does the contraction and
  * the on-the-fly reductions), for benchmarks.  serac_profile_start arms up
- * to max_launches pairs of HIP events; each following launch of that kernel
- * by serac_match_pair, serac_match_pairs or serac_top2_pair is dispatched
- * with hipExtLaunchKernel carrying one pair as its start and stop events
- * (recorded by the dispatch itself on the call's stream, so the launches
- * stay back to back).  serac_profile_stop waits for the recorded events,
- * returns the summed device time in milliseconds and the number of launches
- * timed, and disarms.  Not thread-safe against concurrent matching calls
- * from other threads.
- * Errors: SERAC_ERR_INVALID_ARG (max_launches outside [1, 1048576], NULL
- * outputs, stop without start), SERAC_ERR_HIP.
+ * to max_launches pairs of HIP events; from then on one tile-kernel launch
+ * in `every` (the first, then every `every`-th) made by serac_match_pair,
+ * serac_match_pairs or serac_top2_pair is dispatched with hipExtLaunchKernel
+ * carrying one pair as its start and stop events, recorded by the dispatch
+ * itself on the call's stream.  The event handling slows the enqueueing
+ * host; timing a fraction of the launches keeps the queue as full as
+ * without it.  serac_profile_stop waits for the recorded events, returns
+ * the summed device time in milliseconds and the number of launches timed,
+ * and disarms.  Not thread-safe against concurrent matching calls from
+ * other threads.
+ * Errors: SERAC_ERR_INVALID_ARG (max_launches or every outside
+ * [1, 1048576], NULL outputs, stop without start), SERAC_ERR_HIP.
  */
-int serac_profile_start(int32_t max_launches);
+int serac_profile_start(int32_t max_launches, int32_t every);
 int serac_profile_stop(double *tile_kernel_ms, int32_t *launches);
 
 /* Human-readable text for a status code (static storage). */

@@ -68,7 +68,7 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
                                     ctypes.POINTER(serac_params),
                                     ctypes.POINTER(serac_matches)]
     L.serac_top2_pair.argtypes = [vp, i32, vp, i32, vp, vp, vp]
-    L.serac_profile_start.argtypes = [i32]
+    L.serac_profile_start.argtypes = [i32, i32]
     L.serac_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
     L.serac_status_string.argtypes = [ctypes.c_int]
     L.serac_status_string.restype = ctypes.c_char_p
@@ -180,10 +180,10 @@ def top2(a, b):
     return row, col
 
 
-def profile_start(max_launches: int) -> None:
-    """Time the next max_launches tile-kernel launches with HIP events
-    attached to their dispatches."""
-    rc = library().serac_profile_start(int(max_launches))
+def profile_start(max_launches: int, every: int = 1) -> None:
+    """Time up to max_launches of the following tile-kernel launches, one in
+    `every`, with HIP events attached to their dispatches."""
+    rc = library().serac_profile_start(int(max_launches), int(every))
     if rc != SERAC_OK:
         raise SeracError(rc, "serac_profile_start")
 

@@ -25,8 +25,11 @@
 //     from global memory into LDS (global_load_lds_dwordx4: no registers,
 //     no vector instructions), fetching chunk c+1 into the second buffer
 //     while chunk c is swept.
-//   * A workgroup is four waves, one per SIMD, 128 rows of A by up to 2048
-//     columns of B; two workgroups share a CU.  Each wave keeps the operand
+//   * A workgroup is eight waves, two per SIMD, 256 rows of A by up to 2048
+//     columns of B, one workgroup per CU: the eight waves share every staged
+//     B chunk and the per-chunk barrier keeps them in step (two smaller
+//     workgroups on one CU drift apart, the older one taking the issue
+//     slots, and the younger then finishes alone).  Each wave keeps the operand
 //     fragments of its 32 rows in registers and sweeps 32-column tiles two at
 //     a time, software-pipelined: the MFMAs of one tile pair are issued while
 //     the vector epilogue of the previous pair runs in the same wave, so the
@@ -71,9 +74,10 @@
 namespace {
 
 constexpr int DIM = 128;
-constexpr int TILE_THREADS = 256;       // 4 waves of 64, one per SIMD
+constexpr int TILE_WAVES = 8;           // two per SIMD
+constexpr int TILE_THREADS = 64 * TILE_WAVES;
 constexpr int WAVE_ROWS = 32;           // one 32-row MFMA tile per wave
-constexpr int BLOCK_ROWS = 128;         // rows of A per workgroup
+constexpr int BLOCK_ROWS = WAVE_ROWS * TILE_WAVES;   // rows of A per workgroup
 constexpr int SLICE = 16;               // rows per column tie-break slice
 constexpr int CHUNK = 256;              // columns of B per LDS chunk
 constexpr int CHUNK_BYTES = CHUNK * DIM;
@@ -89,7 +93,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 // One set prepared for the tile kernel (either role or both).
-//   Af  [rowsA/128][4 waves][4 k-slices][64 lanes][16 B]: the MFMA A operand
+//   Af  [rowsA/256][8 waves][4 k-slices][64 lanes][16 B]: the MFMA A operand
 //       of every lane, bytes a ^ 0x80.  Lane (n, h) of wave w holds bytes
 //       [32*kc + 16*h, +16) of wave row q(n) = 16*((n>>2)&1) + 4*(n>>3) + n%4.
 //   RT  [rowsA] row term 128*SA - 2^21.
@@ -208,7 +212,7 @@ __device__ __forceinline__ void prep_body(const PrepJob &Q, int blk)
     const int t = blk * PREP_THREADS + (int)threadIdx.x;
     const int r = t >> 3, part = t & 7;
     if (r >= max(Q.rowsA, Q.rowsB))
-        return;                              // whole rows (rows are multiples of 128)
+        return;                              // whole rows (row counts are multiples of 256)
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     if (r < Q.n)
         v = *reinterpret_cast<const uint4 *>(Q.X + (size_t)r * DIM + 16 * part);
@@ -219,10 +223,10 @@ __device__ __forceinline__ void prep_body(const PrepJob &Q, int blk)
     const uint4 x = make_uint4(v.x ^ 0x80808080u, v.y ^ 0x80808080u, v.z ^ 0x80808080u,
                                v.w ^ 0x80808080u);
     if (r < Q.rowsA) {
-        const int b = r >> 7, w = (r >> 5) & 3, qr = r & 31;
+        const int b = r / BLOCK_ROWS, w = (r % BLOCK_ROWS) / WAVE_ROWS, qr = r & 31;
         const int nn = 8 * ((qr >> 2) & 3) + 4 * (qr >> 4) + (qr & 3);   // q(nn) = qr
         const int kc = part >> 1, hh = part & 1;
-        const size_t off = ((((size_t)b * 4 + w) * 4 + kc) * 64 + 32 * hh + nn) * 16;
+        const size_t off = ((((size_t)b * TILE_WAVES + w) * 4 + kc) * 64 + 32 * hh + nn) * 16;
         *reinterpret_cast<uint4 *>(Q.Af + off) = x;
         if (part == 0)
             Q.RT[r] = (int32_t)(128u * s) - 2097152;
@@ -248,7 +252,7 @@ __global__ __launch_bounds__(PREP_THREADS) void serac_prep_many(const PrepJob *_
 
 // ------------------------------------------------------------ tile sweep
 
-// The fused sweep of one workgroup: 128 rows of A (row block rb) against
+// The fused sweep of one workgroup: 256 rows of A (row block rb) against
 // chunks [c0, c0 + nch) of B.
 //
 // Accumulator layout of the 32x32 MFMA: lane l, register r holds output row
@@ -288,7 +292,8 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     v4i af[4];
     v16i ci;
     {
-        const v4i *pa = reinterpret_cast<const v4i *>(J.Af) + (size_t)(rb * 4 + w) * 256 + lane;
+        const v4i *pa =
+            reinterpret_cast<const v4i *>(J.Af) + (size_t)(rb * TILE_WAVES + w) * 256 + lane;
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc)
             af[kc] = pa[64 * kc];
@@ -844,6 +849,8 @@ Device g_devices[64];
 struct Profile {
     bool armed = false;
     int used = 0;
+    int every = 1;                // time one launch in `every`
+    long long seen = 0;           // tile launches since arming
     std::vector<hipEvent_t> ev;   // [2 * max]: start, stop
 };
 std::mutex g_prof_mutex;
@@ -855,6 +862,8 @@ void prof_slot(hipEvent_t &start, hipEvent_t &stop)
     start = stop = nullptr;
     std::lock_guard<std::mutex> lock(g_prof_mutex);
     if (!g_prof.armed || 2 * (g_prof.used + 1) > (int)g_prof.ev.size())
+        return;
+    if (g_prof.seen++ % g_prof.every != 0)
         return;
     start = g_prof.ev[2 * g_prof.used];
     stop = g_prof.ev[2 * g_prof.used + 1];
@@ -1005,7 +1014,7 @@ struct Plan {
     int units() const { return nRB * Gc; }
 };
 
-// Workgroups of 128 rows by gch chunks of 256 columns; gch (a power of two,
+// Workgroups of 256 rows by gch chunks of 256 columns; gch (a power of two,
 // at most 8, so a workgroup's columns stay inside one aligned 2048-column
 // window) is the largest that still yields about `target` workgroups.
 Plan make_plan(int nA, int nB, long long target)
@@ -1198,7 +1207,7 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int
         serac_zero_counts<<<1, 64, 0, stream>>>(nullptr, out->count, 1);
         return hipGetLastError() == hipSuccess ? SERAC_OK : SERAC_ERR_HIP;
     }
-    const Plan p = make_plan(nA, nB, 2LL * d->cus);
+    const Plan p = make_plan(nA, nB, d->cus);
     Workspace *w = nullptr;
     st = get_workspace(stream, p.acc,
                        p.scratch + prep_bytes(nA, true, false) + prep_bytes(nB, false, true), &w);
@@ -1364,7 +1373,7 @@ int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int3
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     if (nA == 0 && nB == 0)
         return SERAC_OK;
-    const Plan p = make_plan(std::max(nA, 1), std::max(nB, 1), 2LL * d->cus);
+    const Plan p = make_plan(std::max(nA, 1), std::max(nB, 1), d->cus);
     Workspace *w = nullptr;
     st = get_workspace(stream, p.acc,
                        p.scratch + prep_bytes(std::max(nA, 1), true, false) +
@@ -1390,9 +1399,9 @@ int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int3
     return SERAC_OK;
 }
 
-int serac_profile_start(int32_t max_launches)
+int serac_profile_start(int32_t max_launches, int32_t every)
 {
-    if (max_launches < 1 || max_launches > (1 << 20))
+    if (max_launches < 1 || max_launches > (1 << 20) || every < 1 || every > (1 << 20))
         return SERAC_ERR_INVALID_ARG;
     std::lock_guard<std::mutex> lock(g_prof_mutex);
     for (hipEvent_t e : g_prof.ev)
@@ -1400,6 +1409,8 @@ int serac_profile_start(int32_t max_launches)
             (void)hipEventDestroy(e);
     g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
     g_prof.used = 0;
+    g_prof.seen = 0;
+    g_prof.every = every;
     g_prof.armed = false;
     for (auto &e : g_prof.ev) {
         if (hipEventCreate(&e) != hipSuccess) {

@@ -204,3 +204,8 @@ def test_profiled_launches_exact(serac):
     check_pair(serac, p.A, p.B, **p.params(), label="profiled")
     ms, n = serac.profile_stop()
     assert n == 2 and 0.0 < ms < 1000.0      # one match_pair and one top2 launch
+    serac.profile_start(8, 3)                # every third launch: the 1st and the 4th
+    for _ in range(5):
+        serac.match_pair(dev(p.A), dev(p.B), **p.params())
+    ms, n = serac.profile_stop()
+    assert n == 2 and 0.0 < ms < 1000.0
