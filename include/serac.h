@@ -79,8 +79,11 @@ typedef struct serac_match {
 } serac_match;
 
 /* Output of one pair.  matches: device array of capacity entries, filled in
- * ascending order of a; count: device int32 receiving the number written.
- * capacity must be at least nA (each row yields at most one match). */
+ * ascending order of a; count: device int32 receiving the number written,
+ * or -1 if the device-side ordering hand-off between workgroups did not
+ * complete (a bounded wait that only a malfunctioning device exhausts; the
+ * match list is then invalid).  capacity must be at least nA (each row
+ * yields at most one match). */
 typedef struct serac_matches {
     serac_match *matches;
     int64_t capacity;

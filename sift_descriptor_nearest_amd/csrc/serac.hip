@@ -84,10 +84,11 @@ constexpr int CHUNK_BYTES = CHUNK * DIM;
 constexpr int PLANE_BYTES = CHUNK * 16; // one 16-byte part of every column
 constexpr int GROUP_MAX = 2048;         // columns per workgroup: 64 tiles (6-bit index)
 constexpr int MAX_GCH = GROUP_MAX / CHUNK;
+constexpr int SCR_PITCH = 33;           // lane-merge scratch row pitch (entries): reads of one
+                                        // entry from 32 rows fall on distinct banks
 constexpr int PREP_THREADS = 256;
 constexpr int NORM2 = 262144;           // 512^2
 constexpr int GATE_THREADS = 256;
-constexpr int COMPACT_THREADS = 1024;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -115,9 +116,18 @@ struct PrepPair {
     PrepJob q[2];
 };
 
+// Words of the accumulator region the previous call on this stream left
+// raised; the preparation kernel clears them before this call's sweep.
+struct Clear {
+    uint4 *p;
+    size_t words;
+};
+
 // One pair's work description and its accumulators.  The accumulators
-// are zero between calls: the tile kernel raises them with atomic maxima and
-// the finishing kernels read them and clear them again.
+// (column bests, finishing status words) are zero when a sweep starts: the
+// tile kernel raises the column bests with atomic maxima, the finishing
+// kernel reads them and publishes its status words, and the next call's
+// preparation kernel on the stream clears what was left raised.
 struct Job {
     const uint8_t *A;        // raw descriptors (exact tie checks)
     const uint8_t *B;
@@ -131,7 +141,7 @@ struct Job {
     unsigned long long *rslot;  // [Gc][nA] one row result per column group (see pack_slot)
     uint32_t *rs1;              // [nA] best score per row (column export scratch)
     unsigned long long *cbest;  // [nB] (best << 32) | ~slice    (max: lowest slice)
-    int32_t *res;            // [nA] accepted column of each row, or -1 (scratch)
+    unsigned long long *status;  // [ceil(nA / 256)] finishing hand-off (zero before the finish)
     serac_match *out;        // [>= nA]
     int32_t *count;          // 1
 };
@@ -193,6 +203,14 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Workgroup barrier that orders LDS traffic only: waits for this wave's LDS
+// operations, not for its global stores (the release fence of
+// __syncthreads() would wait for those as well).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 typedef __attribute__((address_space(3))) void *lds_void_ptr;
 
 // 16 bytes per lane from global memory straight into LDS: lane l of the
@@ -240,13 +258,24 @@ __device__ __forceinline__ void prep_body(const PrepJob &Q, int blk)
     }
 }
 
-__global__ __launch_bounds__(PREP_THREADS) void serac_prep_pair(PrepPair Q)
+__device__ __forceinline__ void clear_body(const Clear &C)
 {
+    const size_t nthreads = (size_t)gridDim.x * gridDim.y * blockDim.x;
+    for (size_t k = ((size_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+         k < C.words; k += nthreads)
+        C.p[k] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+__global__ __launch_bounds__(PREP_THREADS) void serac_prep_pair(PrepPair Q, Clear C)
+{
+    clear_body(C);
     prep_body(Q.q[blockIdx.y], blockIdx.x);
 }
 
-__global__ __launch_bounds__(PREP_THREADS) void serac_prep_many(const PrepJob *__restrict__ Q)
+__global__ __launch_bounds__(PREP_THREADS) void serac_prep_many(const PrepJob *__restrict__ Q,
+                                                                Clear C)
 {
+    clear_body(C);
     prep_body(Q[blockIdx.y], blockIdx.x);
 }
 
@@ -280,6 +309,7 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     __shared__ __attribute__((aligned(16))) uint8_t sB[2 * CHUNK_BYTES];   // 64 KiB
     __shared__ __attribute__((aligned(16))) uint32_t sP[2 * CHUNK];
     __shared__ uint32_t sCol[COLS ? GROUP_MAX : 1];
+    __shared__ uint2 sScr[TILE_WAVES * WAVE_ROWS * SCR_PITCH];           // 66 KiB, per wave
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -409,16 +439,29 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
 
     // chunk c: pairs 1..3 of the chunk and pair 0 of the next one (pair 0
     // of chunk 0 is issued before the loop)
+    // The two waves of a SIMD take turns at the higher issue priority, one
+    // step each, so that neither runs ahead (with equal priorities the older
+    // wave is always issued first and the other finishes every chunk alone).
+    const bool second = (w >> 2) & 1;        // waves w and w + 4 share a SIMD
+    auto turn = [&](int k) {
+        if (((k & 1) != 0) == second)
+            __builtin_amdgcn_s_setprio(1);
+        else
+            __builtin_amdgcn_s_setprio(0);
+    };
     auto chunk = [&](int c) {
         const int buf = c & 1;
+        turn(1);
         mfma(1);
         epi(0, c, 0, Even{});
         frags(buf, 2, 0);
         schedule(Yes{}, Yes{});
+        turn(2);
         mfma(0);
         epi(1, c, 1, Odd{});
         frags(buf, 3, 1);
         schedule(Yes{}, Yes{});
+        turn(3);
         mfma(1);
         epi(0, c, 2, Even{});
         schedule(Yes{}, No{});
@@ -429,6 +472,7 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
                 stage(c + 2, buf);
             frags(buf ^ 1, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
+            turn(0);
             mfma(0);
             epi(1, c, 3, Odd{});
             frags(buf ^ 1, 1, 1);
@@ -445,38 +489,37 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     for (int c = 0; c < nch; ++c)
         chunk(c);
 
-    // ---- merge the 32 lanes that share each row (via LDS, in the chunk
-    // buffers, now free): lane pair (q, q + 32) folds 16 of the 32 entries of
-    // row q each; key ties (same score, same tile) go to the lower lane,
-    // which is the lower column.
-    __syncthreads();
-    uint2 *scr = reinterpret_cast<uint2 *>(sB) + w * (WAVE_ROWS * 32);
+    __builtin_amdgcn_s_setprio(0);
+    // ---- merge the 32 lanes that share each row, through this wave's own
+    // LDS scratch (no barrier: only this wave writes and reads it): lane pair
+    // (q, q + 32) folds the entries of source lanes 0..15 and 16..31 of row
+    // q in ascending order, so on a key tie (same score, same tile) the
+    // first, lowest lane, which is the lowest column, stays.
+    uint2 *scr = sScr + w * (WAVE_ROWS * SCR_PITCH);
+    uint32_t *wr = reinterpret_cast<uint32_t *>(scr + 16 * h * SCR_PITCH + n);   // row 16h + rr, entry n
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-        const int q = 16 * h + rr;
-        scr[q * 32 + ((n + q) & 31)] = make_uint2(b1[rr], b2[rr]);
+        wr[2 * rr * SCR_PITCH] = b1[rr];               // two 32-bit stores: no register packing
+        wr[2 * rr * SCR_PITCH + 1] = b2[rr];
     }
-    __syncthreads();
+    const uint2 *rd = scr + n * SCR_PITCH + 16 * h;    // row n, entry 16h + k
     uint32_t K1 = 0u, K2 = 0u;
     int L1 = 64;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-        const int src = (16 * h + k) & 31;              // source lane (column)
-        const uint2 e = scr[n * 32 + ((src + n) & 31)];
-        const uint32_t lo = min(K1, e.x);
-        if (e.x > K1 || (e.x == K1 && src < L1))
-            L1 = src;
+        const int src = 16 * h + k;                      // source lane (column)
+        const uint2 e = rd[k];
+        L1 = e.x > K1 ? src : L1;
+        K2 = umax3(min(K1, e.x), K2, e.y);
         K1 = max(K1, e.x);
-        K2 = umax3(lo, K2, e.y);
     }
     {
+        // lane half 0 holds the lower source lanes: it keeps its own on a tie
         const uint32_t o1 = __shfl_xor(K1, 32), o2 = __shfl_xor(K2, 32);
         const int oL = __shfl_xor(L1, 32);
-        const uint32_t lo = min(K1, o1);
-        if (o1 > K1 || (o1 == K1 && oL < L1))
-            L1 = oL;
+        L1 = (o1 > K1 || (h == 1 && o1 == K1)) ? oL : L1;
+        K2 = umax3(min(K1, o1), K2, o2);
         K1 = max(K1, o1);
-        K2 = umax3(lo, K2, o2);
     }
     // publish this row block's top-2 over the workgroup's columns as one
     // packed slot per (row, column group); the gate merges the groups
@@ -489,7 +532,7 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     }
 
     if (COLS) {
-        // every LDS column maximum was raised before the barriers above
+        lds_barrier();                       // every wave's column maxima are in
         const int base = c0 * CHUNK;
         for (int k = tid; k < nch * CHUNK; k += TILE_THREADS) {
             const int col = base + k;
@@ -567,79 +610,40 @@ __device__ __forceinline__ void row_result(const Job &J, int i, uint32_t &S1, in
     S2 = max(sec, loser);
 }
 
-// Ordered compaction of one pair's decisions res[0, nA) into out by one
-// workgroup of GATE_THREADS: rows are taken 32 per thread (8192 per pass), and
-// a workgroup-wide exclusive scan of the per-thread counts places each
-// thread's matches.  Also clears the pair's column accumulators and sets the
-// count.
-__device__ __forceinline__ void compact_pair(const Job &J)
+// Cross-workgroup hand-off of the finishing kernel: one 64-bit status word
+// per gate workgroup, bits 63..62 the state and bits 31..0 a count.
+constexpr unsigned long long ST_OWN = 1ull << 62;        // own match count published
+constexpr unsigned long long ST_INCL = 2ull << 62;       // inclusive prefix published
+constexpr unsigned long long ST_ERR = 3ull << 62;        // look-back gave up
+constexpr int FINISH_SPIN_LIMIT = 1 << 22;
+
+__device__ __forceinline__ unsigned long long status_load(unsigned long long *p)
 {
-    constexpr int PER = 32;
-    constexpr int WAVES = GATE_THREADS / 64;
-    __shared__ int32_t sWave[WAVES];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    int32_t run = 0;
-    for (int base = 0; base < J.nA; base += PER * GATE_THREADS) {
-        const int i0 = base + PER * tid;
-        int32_t v[PER];
-        if (i0 + PER <= J.nA) {
-#pragma unroll
-            for (int q = 0; q < PER / 4; ++q) {
-                const int4 x = *reinterpret_cast<const int4 *>(J.res + i0 + 4 * q);
-                v[4 * q] = x.x;
-                v[4 * q + 1] = x.y;
-                v[4 * q + 2] = x.z;
-                v[4 * q + 3] = x.w;
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < PER; ++k)
-                v[k] = (i0 + k < J.nA) ? J.res[i0 + k] : -1;
-        }
-        int32_t cnt = 0;
-#pragma unroll
-        for (int k = 0; k < PER; ++k)
-            cnt += v[k] >= 0;
-        int32_t inc = cnt;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int32_t t = __shfl_up(inc, d);
-            if (lane >= d)
-                inc += t;
-        }
-        if (lane == 63)
-            sWave[wv] = inc;
-        __syncthreads();
-        int32_t before = 0, total = 0;
-#pragma unroll
-        for (int k = 0; k < WAVES; ++k) {
-            before += (k < wv) ? sWave[k] : 0;
-            total += sWave[k];
-        }
-        int32_t o = run + before + inc - cnt;
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            if (v[k] >= 0) {
-                J.out[o].a = (uint32_t)(i0 + k);
-                J.out[o].b = (uint32_t)v[k];
-                ++o;
-            }
-        }
-        run += total;
-        __syncthreads();                     // sWave reused by the next pass
-    }
-    for (int j = tid; j < J.nB; j += GATE_THREADS)
-        J.cbest[j] = 0ull;
-    if (tid == 0)
-        *J.count = run;
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Gates and cross-check of 256 rows: res[i] = the accepted column of row i,
-// or -1.
-__device__ __forceinline__ void gate_body(const Job &J, int wg, const Gate &G)
+__device__ __forceinline__ void status_store(unsigned long long *p, unsigned long long v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Gates, cross-check and ordered output of 256 rows, one kernel for the
+// whole pair.  Each workgroup decides its rows, publishes its match count
+// and sums the counts of the groups before it (decoupled look-back: a group
+// only waits for groups dispatched before it, so every wait ends), then
+// writes its own matches at that offset.  Only atomic status words cross
+// workgroups, so no device-scope fence (an L2 write-back on gfx950) is
+// needed.  The last group in the chain writes the count.  The column
+// accumulators and the status words are left raised: the next call's
+// preparation kernel on this stream clears them before its sweep.  A
+// look-back that does not see its predecessors within the spin limit marks
+// the pair failed: count -1.
+__device__ __forceinline__ void finish_body(const Job &J, int wg, int nwg, const Gate &G)
 {
     __shared__ uint32_t sS1[GATE_THREADS];
-    const int tid = threadIdx.x;
+    __shared__ int32_t sWave[GATE_THREADS / 64];
+    __shared__ long long sBase;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int i = wg * GATE_THREADS + tid;
     uint32_t S1 = 0u, S2 = 0u;
     int32_t I1 = -1;
@@ -656,8 +660,6 @@ __device__ __forceinline__ void gate_body(const Job &J, int wg, const Gate &G)
             cb = J.cbest[I1];
     }
     __syncthreads();                         // sS1 complete
-    if (i >= J.nA)
-        return;
     bool acc = cand && (d1 <= G.max_distance) && (d1 < G.max_ratio * d2);
     if (acc && G.cross_check) {
         const uint32_t C1 = (uint32_t)(cb >> 32);
@@ -676,96 +678,96 @@ __device__ __forceinline__ void gate_body(const Job &J, int wg, const Gate &G)
             }
         }
     }
-    J.res[i] = acc ? I1 : -1;
+
+    // rank of this row's match inside the group
+    const unsigned long long ball = __ballot(acc);
+    const int in_wave = __popcll(ball & ((1ull << lane) - 1ull));
+    if (lane == 0)
+        sWave[wv] = __popcll(ball);
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int k = 0; k < GATE_THREADS / 64; ++k) {
+        before += k < wv ? sWave[k] : 0;
+        tot += sWave[k];
+    }
+
+    // offset of this group's matches: wave 0 looks back over the groups
+    // before it, 64 status words at a time, folding own counts until the
+    // nearest inclusive prefix
+    unsigned long long *st = J.status;
+    if (wv == 0) {
+        long long base = 0;
+        bool failed = false;
+        if (wg == 0) {
+            if (lane == 0)
+                status_store(st, ST_INCL | (unsigned)tot);
+        } else {
+            if (lane == 0)
+                status_store(st + wg, ST_OWN | (unsigned)tot);
+            int k0 = wg - 1, spins = 0;
+            for (;;) {
+                const int k = k0 - lane;
+                // before group 0 there is an inclusive prefix of 0
+                const unsigned long long v = k >= 0 ? status_load(st + k) : ST_INCL;
+                const unsigned long long state = v & ST_ERR;
+                const unsigned long long incl = __ballot(state == ST_INCL);
+                const int stop = incl ? __ffsll(incl) - 1 : 64;   // nearest inclusive lane
+                const unsigned long long upto = stop >= 63 ? ~0ull : ((2ull << stop) - 1ull);
+                if (__ballot(state == ST_ERR) & upto) {
+                    failed = true;
+                    break;
+                }
+                if (__ballot(state == 0ull) & upto) {
+                    if (++spins > FINISH_SPIN_LIMIT) {
+                        failed = true;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                    continue;
+                }
+                uint32_t c = lane <= stop ? (uint32_t)v : 0u;
+#pragma unroll
+                for (int d = 32; d >= 1; d >>= 1)
+                    c += __shfl_xor(c, d);
+                base += c;
+                if (stop < 64)
+                    break;
+                k0 -= 64;
+            }
+            if (lane == 0)
+                status_store(st + wg, failed ? ST_ERR : (ST_INCL | (unsigned)(base + tot)));
+        }
+        if (lane == 0) {
+            sBase = failed ? -1 : base;
+            if (wg == nwg - 1)
+                *J.count = failed ? -1 : (int32_t)(base + tot);
+        }
+    }
+    __syncthreads();
+    const long long base = sBase;
+    if (acc && base >= 0) {
+        serac_match m;
+        m.a = (uint32_t)i;
+        m.b = (uint32_t)I1;
+        J.out[base + before + in_wave] = m;
+    }
 }
 
-__global__ __launch_bounds__(GATE_THREADS) void serac_gate_one(Job J, Gate G)
+__global__ __launch_bounds__(GATE_THREADS) void serac_finish_one(Job J, Gate G)
 {
-    gate_body(J, blockIdx.x, G);
+    finish_body(J, blockIdx.x, gridDim.x, G);
 }
 
-__global__ __launch_bounds__(GATE_THREADS) void serac_gate_many(const Job *__restrict__ jobs,
-                                                                int gatePerJob, Gate G)
+__global__ __launch_bounds__(GATE_THREADS) void serac_finish_many(const Job *__restrict__ jobs,
+                                                                  int gatePerJob, Gate G)
 {
     const Job J = jobs[blockIdx.x / gatePerJob];
     const int wg = blockIdx.x % gatePerJob;
-    if (wg * GATE_THREADS >= J.nA)
+    const int nwg = (J.nA + GATE_THREADS - 1) / GATE_THREADS;
+    if (wg >= nwg)
         return;
-    gate_body(J, wg, G);
-}
-
-// Ordered compaction of one pair by one workgroup, after all its gate
-// groups: rows are taken 8192 at a time, eight consecutive rows per thread,
-// and a workgroup-wide exclusive scan of the per-thread counts places each
-// thread's matches.  The column accumulators, read by every gate group, are
-// cleared here.  (A single kernel that lets the last gate group compact
-// behind a fence and ticket was measured slower on gfx950: each
-// device-scope fence writes back the XCD's whole L2.)
-__device__ __forceinline__ void compact_body(const Job &J)
-{
-    __shared__ int32_t sWave[COMPACT_THREADS / 64];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    int32_t run = 0;
-    for (int base = 0; base < J.nA; base += 8 * COMPACT_THREADS) {
-        const int i0 = base + 8 * tid;
-        int32_t v[8];
-        if (i0 + 8 <= J.nA) {
-            const int4 lo = *reinterpret_cast<const int4 *>(J.res + i0);
-            const int4 hi = *reinterpret_cast<const int4 *>(J.res + i0 + 4);
-            v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-            v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-        } else {
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                v[k] = (i0 + k < J.nA) ? J.res[i0 + k] : -1;
-        }
-        int32_t cnt = 0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            cnt += v[k] >= 0;
-        int32_t inc = cnt;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int32_t t = __shfl_up(inc, d);
-            if (lane >= d)
-                inc += t;
-        }
-        if (lane == 63)
-            sWave[wv] = inc;
-        __syncthreads();
-        int32_t before = 0, total = 0;
-#pragma unroll
-        for (int k = 0; k < COMPACT_THREADS / 64; ++k) {
-            before += (k < wv) ? sWave[k] : 0;
-            total += sWave[k];
-        }
-        int32_t o = run + before + inc - cnt;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            if (v[k] >= 0) {
-                J.out[o].a = (uint32_t)(i0 + k);
-                J.out[o].b = (uint32_t)v[k];
-                ++o;
-            }
-        }
-        run += total;
-        __syncthreads();                     // sWave reused by the next tile
-    }
-    for (int j = tid; j < J.nB; j += COMPACT_THREADS)
-        J.cbest[j] = 0ull;
-    if (tid == 0)
-        *J.count = run;
-}
-
-__global__ __launch_bounds__(COMPACT_THREADS) void serac_compact_one(Job J)
-{
-    compact_body(J);
-}
-
-__global__ __launch_bounds__(COMPACT_THREADS) void serac_compact_many(const Job *__restrict__ jobs)
-{
-    const Job J = jobs[blockIdx.x];
-    compact_body(J);
+    finish_body(J, wg, nwg, G);
 }
 
 __global__ void serac_zero_counts(int32_t *const *counts, int32_t *count, int n)
@@ -930,15 +932,17 @@ int device_setup(Device **out)
 // order, so consecutive calls on a stream can share one workspace; calls on
 // different streams get different ones.  Growth frees the old buffers and
 // allocates new ones on the same stream, both stream-ordered.
-//   acc  the accumulators of the jobs; all zero between calls (each call
-//        clears what it raised), cleared by a kernel when (re)allocated or
-//        after a failed call;
+//   acc  the accumulators of the jobs; zero when a sweep starts: the
+//        preparation kernel of each call clears the leading acc_used bytes
+//        the previous call left raised; cleared by a kernel when
+//        (re)allocated or after a failed call;
 //   aux  per-call scratch (the job table of a batch).
 struct Workspace {
     int dev;
     hipStream_t stream;
     uint8_t *acc;
     size_t acc_bytes;
+    size_t acc_used;     // leading bytes of acc the last call left raised
     uint8_t *aux;
     size_t aux_bytes;
     bool dirty;
@@ -982,21 +986,38 @@ int get_workspace(hipStream_t stream, size_t acc_bytes, size_t aux_bytes, Worksp
         if (e.dev == dev && e.stream == stream)
             w = &e;
     if (!w) {
-        g_ws.push_back(Workspace{dev, stream, nullptr, 0, nullptr, 0, false});
+        g_ws.push_back(Workspace{dev, stream, nullptr, 0, 0, nullptr, 0, false});
         w = &g_ws.back();
     }
+    const uint8_t *before = w->acc;
     int st = grow(w->acc, w->acc_bytes, acc_bytes, stream, true);
+    if (w->acc != before)
+        w->acc_used = 0;                     // a fresh buffer is cleared
     if (st == SERAC_OK && w->dirty) {
         serac_clear<<<1024, 256, 0, stream>>>(reinterpret_cast<uint4 *>(w->acc),
                                               w->acc_bytes / 16);
         st = hipGetLastError() == hipSuccess ? SERAC_OK : SERAC_ERR_HIP;
-        if (st == SERAC_OK)
+        if (st == SERAC_OK) {
             w->dirty = false;
+            w->acc_used = 0;
+        }
     }
     if (st == SERAC_OK && aux_bytes)
         st = grow(w->aux, w->aux_bytes, aux_bytes, stream, false);
     *out = w;
     return st;
+}
+
+// The part of the accumulators the previous call left raised, for this
+// call's preparation kernel to clear; records what this call will leave.
+Clear take_clear(Workspace *w, size_t leaves)
+{
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Clear C;
+    C.p = reinterpret_cast<uint4 *>(w->acc);
+    C.words = w->acc_used / 16;
+    w->acc_used = leaves;
+    return C;
 }
 
 // A call that enqueued work on the accumulators and then failed may have
@@ -1009,8 +1030,8 @@ void mark_dirty(Workspace *w)
 
 struct Plan {
     int nRB, nBC, gch, Gc;
-    size_t acc;       // bytes of accumulators (zero between calls): cbest
-    size_t scratch;   // bytes of per-call scratch: res / rs1, then rslot
+    size_t acc;       // bytes of accumulators: cbest, then the finishing status words
+    size_t scratch;   // bytes of per-call scratch: rs1, then rslot
     int units() const { return nRB * Gc; }
 };
 
@@ -1027,7 +1048,8 @@ Plan make_plan(int nA, int nB, long long target)
     while (p.gch > 1 && (long long)p.nRB * groups(p.gch) < target)
         p.gch >>= 1;
     p.Gc = groups(p.gch);
-    p.acc = align256((size_t)nB * 8);
+    const size_t gates = (size_t)(nA + GATE_THREADS - 1) / GATE_THREADS;
+    p.acc = align256((size_t)nB * 8) + align256(gates * 8);
     p.scratch = align256((size_t)nA * 4) + align256((size_t)p.Gc * nA * 8);
     return p;
 }
@@ -1094,8 +1116,7 @@ void fill_job(Job &J, const Plan &p, const uint8_t *A, int nA, const PrepJob &QA
     J.gch = p.gch;
     J.Gc = p.Gc;
     J.cbest = reinterpret_cast<unsigned long long *>(acc);
-    // res (matching) and rs1 (export) are never needed in the same call
-    J.res = reinterpret_cast<int32_t *>(scratch);
+    J.status = reinterpret_cast<unsigned long long *>(acc + align256((size_t)nB * 8));
     J.rs1 = reinterpret_cast<uint32_t *>(scratch);
     J.rslot = reinterpret_cast<unsigned long long *>(scratch + align256((size_t)nA * 4));
     J.out = out;
@@ -1151,7 +1172,7 @@ void launch_tiles(const Job &J, const Plan &p, bool cols, hipStream_t stream)
 // Preparation and tile sweep of one pair (nA, nB > 0) on `stream`; the
 // prepared sets go to `prep` (prep_bytes(nA, 1, 0) + prep_bytes(nB, 0, 1)).
 void launch_pair(Job &J, const Plan &p, const uint8_t *A, int nA, const uint8_t *B, int nB,
-                 uint8_t *prep, bool cols, hipStream_t stream)
+                 uint8_t *prep, const Clear &C, bool cols, hipStream_t stream)
 {
     uint8_t *q = prep;
     PrepPair Q;
@@ -1162,7 +1183,7 @@ void launch_pair(Job &J, const Plan &p, const uint8_t *A, int nA, const uint8_t 
     J.Bp = Q.q[1].Bp;
     J.P = Q.q[1].P;
     const dim3 pg(std::max(prep_blocks(Q.q[0]), prep_blocks(Q.q[1])), 2);
-    serac_prep_pair<<<pg, PREP_THREADS, 0, stream>>>(Q);
+    serac_prep_pair<<<pg, PREP_THREADS, 0, stream>>>(Q, C);
     launch_tiles(J, p, cols, stream);
 }
 
@@ -1216,11 +1237,10 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int
     Job J;
     const PrepJob none{};
     fill_job(J, p, descA, nA, none, descB, nB, none, w->acc, w->aux, out->matches, out->count);
-    launch_pair(J, p, descA, nA, descB, nB, w->aux + p.scratch, params->cross_check != 0,
-                stream);
+    launch_pair(J, p, descA, nA, descB, nB, w->aux + p.scratch, take_clear(w, p.acc),
+                params->cross_check != 0, stream);
     const Gate G = make_gate(d, params);
-    serac_gate_one<<<(nA + GATE_THREADS - 1) / GATE_THREADS, GATE_THREADS, 0, stream>>>(J, G);
-    serac_compact_one<<<1, COMPACT_THREADS, 0, stream>>>(J);
+    serac_finish_one<<<(nA + GATE_THREADS - 1) / GATE_THREADS, GATE_THREADS, 0, stream>>>(J, G);
     if (hipGetLastError() != hipSuccess) {
         mark_dirty(w);
         return SERAC_ERR_HIP;
@@ -1333,7 +1353,7 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
                                                                          (int)zero.size());
     if (e == hipSuccess && nlive) {
         serac_prep_many<<<dim3(prepBlocks, (unsigned)prepped.size()), PREP_THREADS, 0, stream>>>(
-            dpjobs);
+            dpjobs, take_clear(w, acc_bytes));
         const Gate G = make_gate(d, params);
         hipEvent_t e0, e1;
         prof_slot(e0, e1);
@@ -1344,8 +1364,8 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
         else
             hipExtLaunchKernelGGL(serac_tiles_many<false>, grid, dim3(TILE_THREADS), 0, stream,
                                   e0, e1, 0, djobs, unitsPerJob);
-        serac_gate_many<<<nlive * gatePerJob, GATE_THREADS, 0, stream>>>(djobs, gatePerJob, G);
-        serac_compact_many<<<nlive, COMPACT_THREADS, 0, stream>>>(djobs);
+        serac_finish_many<<<nlive * gatePerJob, GATE_THREADS, 0, stream>>>(djobs, gatePerJob,
+                                                                          G);
     }
     if (e == hipSuccess)
         e = hipGetLastError();
@@ -1387,7 +1407,9 @@ int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int3
     // with an empty side nothing is raised: rows report (0, -1, 0) and
     // columns (0, -1) from the cleared accumulators
     if (nA > 0 && nB > 0)
-        launch_pair(J, p, descA, nA, descB, nB, w->aux + p.scratch, true, stream);
+        // the export clears the column accumulators: nothing stays raised
+        launch_pair(J, p, descA, nA, descB, nB, w->aux + p.scratch, take_clear(w, 0), true,
+                    stream);
     if (nA > 0)
         serac_export_rows<<<(nA + 255) / 256, 256, 0, stream>>>(J, row_top2);
     if (nB > 0)
