@@ -81,6 +81,8 @@ def main() -> int:
     ap.add_argument("--workload", default="pair_8192x8192")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-every", type=int, default=PROFILE_EVERY, metavar="K",
+                    help="attach timing events to one tile-kernel launch in K")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, copy a MIB-MiB device buffer 10 times "
                          "(a plain copy kernel of known traffic, for scaling the "
@@ -127,7 +129,8 @@ def main() -> int:
 
     # the dominant kernel's launch duration, live in the timed region: HIP
     # events attached to one tile-kernel dispatch in PROFILE_EVERY
-    serac.profile_start(args.steps // PROFILE_EVERY + 1, PROFILE_EVERY)
+    every = max(1, args.profile_every)
+    serac.profile_start(args.steps // every + 1, every)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):

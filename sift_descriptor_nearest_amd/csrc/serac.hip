@@ -216,9 +216,18 @@ typedef __attribute__((address_space(3))) void *lds_void_ptr;
 // 16 bytes per lane from global memory straight into LDS: lane l of the
 // wave writes bytes [16*l, 16*l + 16) after `lds_wave_base`, which must be
 // the same for the whole wave.
+//
+// Issued as inline assembly so that the compiler does not track the LDS
+// write: it cannot tell the two chunk buffers apart and would otherwise
+// wait for the prefetch of the next chunk before every LDS access that
+// follows it.  Callers order the write themselves (wait_vmcnt, barrier);
+// the compiler's own vmcnt waits stay safe, as extra loads in flight only
+// make them wait longer.
 __device__ __forceinline__ void load_lds16(const void *src, void *lds_wave_base)
 {
-    __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)lds_wave_base, 16, 0, 0);
+    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void_ptr)lds_wave_base;
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(m0) : "memory", "m0");
 }
 
 // ------------------------------------------------------------ preparation
@@ -610,6 +619,34 @@ __device__ __forceinline__ void row_result(const Job &J, int i, uint32_t &S1, in
     S2 = max(sec, loser);
 }
 
+// Row results of the lane `D` places lower in the same 16-lane row (one
+// 16-row slice), `fill` where there is none.
+template <int D>
+__device__ __forceinline__ uint32_t slice_below(uint32_t v, uint32_t fill)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)v, 0x110 | D, 0xF, 0xF, false);
+}
+
+// Column-tie test of the cross-check for a row whose best score S1 equals
+// its column's maximum C1: a lower row i2 of the slice scores S(i2, I1) <=
+// S1(i2); when I1 is i2's best column S(i2, I1) = S1(i2) (a tie when equal
+// to C1), and otherwise S(i2, I1) <= S2(i2), so the exact product is needed
+// only when S1(i2) and S2(i2) both reach C1 (bit D of `dots`).  All lanes
+// of the wave take part.
+template <int D>
+__device__ __forceinline__ void slice_ties(uint32_t S1, uint32_t S2, int32_t I1, uint32_t C1,
+                                           bool &tie, uint32_t &dots)
+{
+    const uint32_t s1 = slice_below<D>(S1, 0u);
+    const uint32_t s2 = slice_below<D>(S2, 0u);
+    const int32_t i1 = (int32_t)slice_below<D>((uint32_t)I1, 0xFFFFFFFFu);
+    const bool same = i1 == I1;
+    tie = tie | (same & (s1 == C1));
+    dots |= (uint32_t)(!same & (s1 >= C1) & (s2 >= C1)) << D;
+    if constexpr (D < SLICE - 1)
+        slice_ties<D + 1>(S1, S2, I1, C1, tie, dots);
+}
+
 // Cross-workgroup hand-off of the finishing kernel: one 64-bit status word
 // per gate workgroup, bits 63..62 the state and bits 31..0 a count.
 constexpr unsigned long long ST_OWN = 1ull << 62;        // own match count published
@@ -640,7 +677,6 @@ __device__ __forceinline__ void status_store(unsigned long long *p, unsigned lon
 // the pair failed: count -1.
 __device__ __forceinline__ void finish_body(const Job &J, int wg, int nwg, const Gate &G)
 {
-    __shared__ uint32_t sS1[GATE_THREADS];
     __shared__ int32_t sWave[GATE_THREADS / 64];
     __shared__ long long sBase;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -649,7 +685,6 @@ __device__ __forceinline__ void finish_body(const Job &J, int wg, int nwg, const
     int32_t I1 = -1;
     if (i < J.nA)
         row_result(J, i, S1, I1, S2);
-    sS1[tid] = S1;
     const bool cand = I1 >= 0 && I1 < J.nB;
     double d1 = 0.0, d2 = 0.0;
     unsigned long long cb = 0ull;
@@ -659,22 +694,25 @@ __device__ __forceinline__ void finish_body(const Job &J, int wg, int nwg, const
         if (G.cross_check)
             cb = J.cbest[I1];
     }
-    __syncthreads();                         // sS1 complete
     bool acc = cand && (d1 <= G.max_distance) && (d1 < G.max_ratio * d2);
-    if (acc && G.cross_check) {
+    if (G.cross_check) {
         const uint32_t C1 = (uint32_t)(cb >> 32);
         const int32_t slice = (int32_t)(0xFFFFFFFFu - (uint32_t)cb);
-        if (C1 != S1 || slice != i / SLICE) {
-            acc = false;
-        } else {
-            // a lower row of the same slice reaching the same score wins
-            const uint8_t *b = J.B + (size_t)I1 * DIM;
-            for (int i2 = i - i % SLICE; i2 < i; ++i2) {
-                if (sS1[i2 - wg * GATE_THREADS] >= C1 &&
-                    (uint32_t)dot_exact(J.A + (size_t)i2 * DIM, b) == C1) {
+        acc = acc && C1 == S1 && slice == i / SLICE;
+        // Row i is its column's best only if no lower row of its 16-row
+        // slice (the lanes below it in its 16-lane row) reaches C1 on that
+        // column too; tested in registers for the whole wave at once.
+        if (__ballot(acc) != 0ull) {
+            bool tie = false;
+            uint32_t dots = 0u;
+            slice_ties<1>(S1, S2, I1, C1, tie, dots);
+            acc = acc && !tie;
+            const uint8_t *b = J.B + (size_t)max(I1, 0) * DIM;
+            while (acc && dots != 0u) {
+                const int d = __ffs(dots) - 1;
+                dots &= dots - 1u;
+                if ((uint32_t)dot_exact(J.A + (size_t)(i - d) * DIM, b) == C1)
                     acc = false;
-                    break;
-                }
             }
         }
     }
