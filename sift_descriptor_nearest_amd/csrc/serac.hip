@@ -84,8 +84,7 @@ constexpr int CHUNK_BYTES = CHUNK * DIM;
 constexpr int PLANE_BYTES = CHUNK * 16; // one 16-byte part of every column
 constexpr int GROUP_MAX = 2048;         // columns per workgroup: 64 tiles (6-bit index)
 constexpr int MAX_GCH = GROUP_MAX / CHUNK;
-constexpr int SCR_PITCH = 33;           // lane-merge scratch row pitch (entries): reads of one
-                                        // entry from 32 rows fall on distinct banks
+constexpr int SCR_WAVE = WAVE_ROWS * 32;  // lane-merge scratch entries per wave (32 rows x 32)
 constexpr int PREP_THREADS = 256;
 constexpr int NORM2 = 262144;           // 512^2
 constexpr int GATE_THREADS = 256;
@@ -117,10 +116,12 @@ struct PrepPair {
 };
 
 // Words of the accumulator region the previous call on this stream left
-// raised; the preparation kernel clears them before this call's sweep.
+// raised; the first kernel of this call clears them, `stride` threads of it
+// (the blocks of its first grid row).
 struct Clear {
     uint4 *p;
     size_t words;
+    uint32_t stride;
 };
 
 // One pair's work description and its accumulators.  The accumulators
@@ -170,6 +171,10 @@ __host__ __device__ __forceinline__ unsigned long long pack_slot(uint32_t S1, ui
     return ((unsigned long long)S1 << 41) |
            ((unsigned long long)(SLOT_COL_MAX - col) << 23) | (unsigned long long)S2;
 }
+
+// 128 zero bytes: the descriptor a fused sweep reads for columns past the end
+// of B (an all-zero descriptor scores 0 against anything).
+__device__ const uint8_t g_zero_desc[DIM] = {};
 
 __device__ __forceinline__ uint32_t umax3(uint32_t a, uint32_t b, uint32_t c)
 {
@@ -267,24 +272,27 @@ __device__ __forceinline__ void prep_body(const PrepJob &Q, int blk)
     }
 }
 
+// (The block size is a template argument: reading blockDim or gridDim costs
+// a load from the dispatch packet at kernel start.)
+template <int BS>
 __device__ __forceinline__ void clear_body(const Clear &C)
 {
-    const size_t nthreads = (size_t)gridDim.x * gridDim.y * blockDim.x;
-    for (size_t k = ((size_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
-         k < C.words; k += nthreads)
+    if (blockIdx.y != 0)
+        return;
+    for (size_t k = (size_t)blockIdx.x * BS + threadIdx.x; k < C.words; k += C.stride)
         C.p[k] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 __global__ __launch_bounds__(PREP_THREADS) void serac_prep_pair(PrepPair Q, Clear C)
 {
-    clear_body(C);
+    clear_body<PREP_THREADS>(C);
     prep_body(Q.q[blockIdx.y], blockIdx.x);
 }
 
 __global__ __launch_bounds__(PREP_THREADS) void serac_prep_many(const PrepJob *__restrict__ Q,
                                                                 Clear C)
 {
-    clear_body(C);
+    clear_body<PREP_THREADS>(C);
     prep_body(Q[blockIdx.y], blockIdx.x);
 }
 
@@ -312,13 +320,24 @@ __global__ __launch_bounds__(PREP_THREADS) void serac_prep_many(const PrepJob *_
 // Each workgroup writes, per row and column group, one packed slot (best,
 // column, second) with a plain store, and raises the column best of its
 // columns with 64-bit atomic maxima; nothing is read back.
-template <bool COLS>
+//
+// FUSED sweeps read the raw descriptors and convert them on the way (what
+// the preparation kernel does otherwise): the wave's A operands and row
+// terms in the prologue, and each chunk of B in two stages, a copy of the
+// raw chunk into LDS and, during the chunk before the one that needs it,
+// its conversion into the operand planes and the columns' key addends.
+template <bool COLS, bool FUSED>
 __device__ __forceinline__ void tiles_body(const Job &J, int u)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t sB[2 * CHUNK_BYTES];   // 64 KiB
+    // chunk buffers (operand planes), and for a fused sweep the raw chunk
+    __shared__ __attribute__((aligned(16))) uint8_t sB[(FUSED ? 3 : 2) * CHUNK_BYTES];
     __shared__ __attribute__((aligned(16))) uint32_t sP[2 * CHUNK];
     __shared__ uint32_t sCol[COLS ? GROUP_MAX : 1];
-    __shared__ uint2 sScr[TILE_WAVES * WAVE_ROWS * SCR_PITCH];           // 66 KiB, per wave
+    // lane-merge scratch, 8 KiB per wave; a fused sweep merges in the LDS
+    // its chunks no longer use
+    __shared__ uint2 sScr[FUSED ? 1 : TILE_WAVES * SCR_WAVE];
+    __shared__ __attribute__((aligned(16))) int32_t sRT[FUSED ? BLOCK_ROWS : 1];
+    uint8_t *const sRaw = sB + 2 * CHUNK_BYTES;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -327,10 +346,80 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     const int c0 = cg * J.gch;
     const int nch = min(J.gch, J.nBC - c0);
 
+    // ---- fused sweep: raw chunk copy (contiguous, like the chunk itself) and
+    // its conversion.  Each wave converts only bytes it copied itself (no
+    // barrier needed): lane l takes half l&1 of column 64*(l>>4) + 8*w +
+    // ((l>>1)&7).
+    const int hf = lane & 1;
+    const int hcol = 64 * (lane >> 4) + 8 * w + ((lane >> 1) & 7);
+    auto fetch_raw = [&](int c) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int off = k * (TILE_THREADS * 16) + tid * 16;    // byte of the chunk
+            const int col = (c0 + c) * CHUNK + off / DIM;
+            const uint8_t *src = col < J.nB ? J.B + (size_t)col * DIM + off % DIM
+                                            : g_zero_desc + off % DIM;
+            load_lds16(src, sRaw + k * (TILE_THREADS * 16) + w * 1024);
+        }
+    };
+    auto convert = [&](int c, int buf) {
+        uint4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            v[k] = *reinterpret_cast<const uint4 *>(sRaw + hcol * DIM + 64 * hf + 16 * k);
+        uint32_t sum = 0u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            sum += bytesum16(v[k]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            *reinterpret_cast<uint4 *>(sB + buf * CHUNK_BYTES + (4 * hf + k) * PLANE_BYTES +
+                                       hcol * 16) =
+                make_uint4(v[k].x ^ 0x80808080u, v[k].y ^ 0x80808080u, v[k].z ^ 0x80808080u,
+                           v[k].w ^ 0x80808080u);
+        // the other half of the column is in the neighbouring lane
+        sum += (uint32_t)__builtin_amdgcn_mov_dpp((int)sum, 0xB1, 0xF, 0xF, false);
+        const int col = (c0 + c) * CHUNK + hcol;
+        if (hf == 0)
+            sP[buf * CHUNK + hcol] = ((128u * sum) << 9) + (uint32_t)(511 - ((col >> 5) & 63));
+    };
+
     // ---- this wave's rows of A: operand fragments and the row terms
     v4i af[4];
     v16i ci;
-    {
+    if (FUSED) {
+        fetch_raw(0);
+        // lane (n, h) holds bytes [32*kc + 16*h, +16) of wave row q(n)
+        const int qn = 16 * ((n >> 2) & 1) + 4 * (n >> 3) + (n & 3);
+        const int row = rb * BLOCK_ROWS + w * WAVE_ROWS + qn;
+        const uint8_t *ra = (row < J.nA ? J.A + (size_t)row * DIM : g_zero_desc) + 16 * h;
+        uint4 v4[4];
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+            v4[kc] = *reinterpret_cast<const uint4 *>(ra + 32 * kc);
+        uint32_t sa = 0u;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            const uint4 v = v4[kc];
+            sa += bytesum16(v);
+            af[kc] = (v4i){(int)(v.x ^ 0x80808080u), (int)(v.y ^ 0x80808080u),
+                           (int)(v.z ^ 0x80808080u), (int)(v.w ^ 0x80808080u)};
+        }
+        sa += __shfl_xor(sa, 32);             // the row's other 64 bytes
+        // row terms into the C-input order: lane half h, register r <- wave
+        // row 16*h + r (through this wave's slice of sRT)
+        if (h == 0)
+            sRT[w * WAVE_ROWS + qn] = (int32_t)(128u * sa) - 2097152;
+        __builtin_amdgcn_wave_barrier();
+        const v4i *pr = reinterpret_cast<const v4i *>(sRT + w * WAVE_ROWS + 16 * h);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const v4i x = pr[g];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ci[4 * g + e] = x[e];
+        }
+    } else {
         const v4i *pa =
             reinterpret_cast<const v4i *>(J.Af) + (size_t)(rb * TILE_WAVES + w) * 256 + lane;
 #pragma unroll
@@ -347,7 +436,7 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
         }
     }
 
-    // ---- chunk staging: 8 + (wave 0) 1 loads per thread
+    // ---- chunk staging of prepared sets: 8 + (wave 0) 1 loads per thread
     auto stage = [&](int c, int buf) {
         const uint8_t *src = J.Bp + (size_t)(c0 + c) * CHUNK_BYTES + tid * 16;
         uint8_t *dst = sB + buf * CHUNK_BYTES + w * 1024;
@@ -357,14 +446,22 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
         if (w == 0)
             load_lds16(J.P + (size_t)(c0 + c) * CHUNK + lane * 4, sP + buf * CHUNK);
     };
-    stage(0, 0);
+    if (!FUSED)
+        stage(0, 0);
     if (COLS) {
         for (int k = tid; k < nch * CHUNK; k += TILE_THREADS)
             sCol[k] = 0u;
     }
     wait_vmcnt<0>();                         // chunk 0 and the A operands landed
+    if (FUSED) {
+        convert(0, 0);
+        if (nch > 1) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): raw chunk 0 read back
+            fetch_raw(1);
+        }
+    }
     __syncthreads();
-    if (nch > 1)
+    if (!FUSED && nch > 1)
         stage(1, 1);                         // needed one chunk from now
 
     v4i bf[2][4];        // [tile][k-slice]: operands of the next pair
@@ -465,6 +562,17 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
         epi(0, c, 0, Even{});
         frags(buf, 2, 0);
         schedule(Yes{}, Yes{});
+        if (FUSED && c + 1 < nch) {
+            // chunk c+1 into the buffer chunk c-1 used; the raw copy of
+            // chunk c+2 follows as soon as this thread's part is read back
+            wait_vmcnt<0>();
+            convert(c + 1, buf ^ 1);
+            if (c + 2 < nch) {
+                __builtin_amdgcn_s_waitcnt(0xC07F);
+                fetch_raw(c + 2);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         turn(2);
         mfma(0);
         epi(1, c, 1, Odd{});
@@ -475,9 +583,10 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
         epi(0, c, 2, Even{});
         schedule(Yes{}, No{});
         if (c + 1 < nch) {
-            wait_vmcnt<0>();                 // chunk c+1 landed (this wave's part)
+            if (!FUSED)
+                wait_vmcnt<0>();             // chunk c+1 landed (this wave's part)
             __syncthreads();                 // ... all parts; chunk c no longer read
-            if (c + 2 < nch)
+            if (!FUSED && c + 2 < nch)
                 stage(c + 2, buf);
             frags(buf ^ 1, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
@@ -504,20 +613,30 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     // (q, q + 32) folds the entries of source lanes 0..15 and 16..31 of row
     // q in ascending order, so on a key tie (same score, same tile) the
     // first, lowest lane, which is the lowest column, stays.
-    uint2 *scr = sScr + w * (WAVE_ROWS * SCR_PITCH);
-    uint32_t *wr = reinterpret_cast<uint32_t *>(scr + 16 * h * SCR_PITCH + n);   // row 16h + rr, entry n
+    // Entry e of row r sits at r*32 + (e ^ r): the stores of one row and the
+    // loads of one entry from 32 rows both fall on distinct banks.  A fused
+    // sweep uses the 64 KiB its chunks left free (every wave is past the last
+    // chunk barrier): the buffer of chunk nch-2 for waves 0..3, the raw copy
+    // for waves 4..7.
+    uint2 *scr;
+    if (FUSED)
+        scr = reinterpret_cast<uint2 *>((w < 4 ? sB + (nch & 1) * CHUNK_BYTES : sRaw)) +
+              (w & 3) * SCR_WAVE;
+    else
+        scr = sScr + w * SCR_WAVE;
+    uint32_t *wr = reinterpret_cast<uint32_t *>(scr);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-        wr[2 * rr * SCR_PITCH] = b1[rr];               // two 32-bit stores: no register packing
-        wr[2 * rr * SCR_PITCH + 1] = b2[rr];
+        const int r = 16 * h + rr;                     // row r, entry n
+        wr[2 * (r * 32 + (n ^ r))] = b1[rr];           // two 32-bit stores: no register packing
+        wr[2 * (r * 32 + (n ^ r)) + 1] = b2[rr];
     }
-    const uint2 *rd = scr + n * SCR_PITCH + 16 * h;    // row n, entry 16h + k
     uint32_t K1 = 0u, K2 = 0u;
     int L1 = 64;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         const int src = 16 * h + k;                      // source lane (column)
-        const uint2 e = rd[k];
+        const uint2 e = scr[n * 32 + (src ^ n)];         // row n, entry src
         L1 = e.x > K1 ? src : L1;
         K2 = umax3(min(K1, e.x), K2, e.y);
         K1 = max(K1, e.x);
@@ -559,7 +678,17 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
 template <bool COLS>
 __global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_one(Job J)
 {
-    tiles_body<COLS>(J, blockIdx.x);
+    tiles_body<COLS, false>(J, blockIdx.x);
+}
+
+// One pair straight from the raw descriptors (no preparation kernel); also
+// clears what the previous call on the stream left raised (the other
+// accumulator region, which this call does not touch).
+template <bool COLS>
+__global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_fused(Job J, Clear C)
+{
+    clear_body<TILE_THREADS>(C);
+    tiles_body<COLS, true>(J, blockIdx.x);
 }
 
 template <bool COLS>
@@ -570,7 +699,7 @@ __global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_many(const Job *_
     const int u = blockIdx.x % unitsPerJob;
     if (u >= J.nRB * J.Gc)
         return;
-    tiles_body<COLS>(J, u);
+    tiles_body<COLS, false>(J, u);
 }
 
 // Exact inner product of two descriptors (used only to settle column ties
@@ -794,7 +923,7 @@ __device__ __forceinline__ void finish_body(const Job &J, int wg, int nwg, const
 
 __global__ __launch_bounds__(GATE_THREADS) void serac_finish_one(Job J, Gate G)
 {
-    finish_body(J, blockIdx.x, gridDim.x, G);
+    finish_body(J, blockIdx.x, (J.nA + GATE_THREADS - 1) / GATE_THREADS, G);
 }
 
 __global__ __launch_bounds__(GATE_THREADS) void serac_finish_many(const Job *__restrict__ jobs,
@@ -970,17 +1099,20 @@ int device_setup(Device **out)
 // order, so consecutive calls on a stream can share one workspace; calls on
 // different streams get different ones.  Growth frees the old buffers and
 // allocates new ones on the same stream, both stream-ordered.
-//   acc  the accumulators of the jobs; zero when a sweep starts: the
-//        preparation kernel of each call clears the leading acc_used bytes
-//        the previous call left raised; cleared by a kernel when
-//        (re)allocated or after a failed call;
-//   aux  per-call scratch (the job table of a batch).
+//   acc  the accumulators of the jobs, in two equal regions that calls use
+//        in turn; a call's region is zero when it starts: the first kernel
+//        of each call clears the leading bytes the previous call left
+//        raised in the other region (which this call does not touch); the
+//        whole buffer is cleared by a kernel when (re)allocated or after a
+//        failed call;
+//   aux  per-call scratch (the job table of a batch, prepared sets).
 struct Workspace {
     int dev;
     hipStream_t stream;
     uint8_t *acc;
-    size_t acc_bytes;
-    size_t acc_used;     // leading bytes of acc the last call left raised
+    size_t acc_bytes;    // both regions
+    size_t acc_used[2];  // leading bytes of each region the last call on it left raised
+    int region;          // the region the next call uses (zero)
     uint8_t *aux;
     size_t aux_bytes;
     bool dirty;
@@ -1024,20 +1156,24 @@ int get_workspace(hipStream_t stream, size_t acc_bytes, size_t aux_bytes, Worksp
         if (e.dev == dev && e.stream == stream)
             w = &e;
     if (!w) {
-        g_ws.push_back(Workspace{dev, stream, nullptr, 0, 0, nullptr, 0, false});
+        g_ws.push_back(Workspace{dev, stream, nullptr, 0, {0, 0}, 0, nullptr, 0, false});
         w = &g_ws.back();
     }
     const uint8_t *before = w->acc;
-    int st = grow(w->acc, w->acc_bytes, acc_bytes, stream, true);
-    if (w->acc != before)
-        w->acc_used = 0;                     // a fresh buffer is cleared
+    // two regions of at least acc_bytes each (grow's minimum keeps halves
+    // 256-byte aligned)
+    int st = grow(w->acc, w->acc_bytes, 2 * align256(acc_bytes), stream, true);
+    if (w->acc != before) {
+        w->acc_used[0] = w->acc_used[1] = 0;   // a fresh buffer is cleared
+        w->region = 0;
+    }
     if (st == SERAC_OK && w->dirty) {
         serac_clear<<<1024, 256, 0, stream>>>(reinterpret_cast<uint4 *>(w->acc),
                                               w->acc_bytes / 16);
         st = hipGetLastError() == hipSuccess ? SERAC_OK : SERAC_ERR_HIP;
         if (st == SERAC_OK) {
             w->dirty = false;
-            w->acc_used = 0;
+            w->acc_used[0] = w->acc_used[1] = 0;
         }
     }
     if (st == SERAC_OK && aux_bytes)
@@ -1046,15 +1182,27 @@ int get_workspace(hipStream_t stream, size_t acc_bytes, size_t aux_bytes, Worksp
     return st;
 }
 
-// The part of the accumulators the previous call left raised, for this
-// call's preparation kernel to clear; records what this call will leave.
+// The accumulator region of the next call (zero).
+uint8_t *next_region(Workspace *w)
+{
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    return w->acc + (size_t)w->region * (w->acc_bytes / 2);
+}
+
+// Takes the next region for this call: returns what the previous call left
+// raised in the other region, for this call's first kernel to clear, and
+// records what this call will leave in its own.
 Clear take_clear(Workspace *w, size_t leaves)
 {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
+    const int cur = w->region, other = 1 - cur;
     Clear C;
-    C.p = reinterpret_cast<uint4 *>(w->acc);
-    C.words = w->acc_used / 16;
-    w->acc_used = leaves;
+    C.stride = 1;                            // set by the launch
+    C.p = reinterpret_cast<uint4 *>(w->acc + (size_t)other * (w->acc_bytes / 2));
+    C.words = w->acc_used[other] / 16;
+    w->acc_used[other] = 0;
+    w->acc_used[cur] = leaves;
+    w->region = other;
     return C;
 }
 
@@ -1207,11 +1355,45 @@ void launch_tiles(const Job &J, const Plan &p, bool cols, hipStream_t stream)
     }
 }
 
-// Preparation and tile sweep of one pair (nA, nB > 0) on `stream`; the
-// prepared sets go to `prep` (prep_bytes(nA, 1, 0) + prep_bytes(nB, 0, 1)).
-void launch_pair(Job &J, const Plan &p, const uint8_t *A, int nA, const uint8_t *B, int nB,
-                 uint8_t *prep, const Clear &C, bool cols, hipStream_t stream)
+// A pair small enough that converting the raw descriptors inside the sweep
+// (every workgroup converts the chunks it reads) costs less than the
+// separate preparation kernel and the launch boundary after it.
+constexpr long long FUSED_MAX_WORK = 1ll << 27;    // nA * nB
+
+bool fused_pair(int nA, int nB)
 {
+    return (long long)nA * nB <= FUSED_MAX_WORK;
+}
+
+// Bytes of prepared sets one pair needs (none for a fused sweep).
+size_t pair_prep_bytes(int nA, int nB)
+{
+    return fused_pair(nA, nB) ? 0 : prep_bytes(nA, true, false) + prep_bytes(nB, false, true);
+}
+
+// Preparation and tile sweep of one pair (nA, nB > 0) on `stream`; the
+// prepared sets go to `prep` (pair_prep_bytes(nA, nB)).
+void launch_pair(Job &J, const Plan &p, const uint8_t *A, int nA, const uint8_t *B, int nB,
+                 uint8_t *prep, Clear C, bool cols, hipStream_t stream)
+{
+    if (fused_pair(nA, nB)) {
+        C.stride = (uint32_t)p.units() * TILE_THREADS;
+        hipEvent_t e0, e1;
+        prof_slot(e0, e1);
+        if (e0) {
+            if (cols)
+                hipExtLaunchKernelGGL(serac_tiles_fused<true>, dim3(p.units()),
+                                      dim3(TILE_THREADS), 0, stream, e0, e1, 0, J, C);
+            else
+                hipExtLaunchKernelGGL(serac_tiles_fused<false>, dim3(p.units()),
+                                      dim3(TILE_THREADS), 0, stream, e0, e1, 0, J, C);
+        } else if (cols) {
+            serac_tiles_fused<true><<<p.units(), TILE_THREADS, 0, stream>>>(J, C);
+        } else {
+            serac_tiles_fused<false><<<p.units(), TILE_THREADS, 0, stream>>>(J, C);
+        }
+        return;
+    }
     uint8_t *q = prep;
     PrepPair Q;
     Q.q[0] = make_prep(A, nA, true, false, q);
@@ -1221,6 +1403,7 @@ void launch_pair(Job &J, const Plan &p, const uint8_t *A, int nA, const uint8_t 
     J.Bp = Q.q[1].Bp;
     J.P = Q.q[1].P;
     const dim3 pg(std::max(prep_blocks(Q.q[0]), prep_blocks(Q.q[1])), 2);
+    C.stride = pg.x * PREP_THREADS;
     serac_prep_pair<<<pg, PREP_THREADS, 0, stream>>>(Q, C);
     launch_tiles(J, p, cols, stream);
 }
@@ -1268,13 +1451,13 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int
     }
     const Plan p = make_plan(nA, nB, d->cus);
     Workspace *w = nullptr;
-    st = get_workspace(stream, p.acc,
-                       p.scratch + prep_bytes(nA, true, false) + prep_bytes(nB, false, true), &w);
+    st = get_workspace(stream, p.acc, p.scratch + pair_prep_bytes(nA, nB), &w);
     if (st != SERAC_OK)
         return st;
     Job J;
     const PrepJob none{};
-    fill_job(J, p, descA, nA, none, descB, nB, none, w->acc, w->aux, out->matches, out->count);
+    fill_job(J, p, descA, nA, none, descB, nB, none, next_region(w), w->aux, out->matches,
+             out->count);
     launch_pair(J, p, descA, nA, descB, nB, w->aux + p.scratch, take_clear(w, p.acc),
                 params->cross_check != 0, stream);
     const Gate G = make_gate(d, params);
@@ -1371,7 +1554,7 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
         slot[im] = (int)k;
         prepBlocks = std::max(prepBlocks, prep_blocks(pjobs[k]));
     }
-    uint8_t *q = w->acc;
+    uint8_t *q = next_region(w);
     for (int k = 0; k < nlive; ++k) {
         const serac_pair pr = pairs[live[k]];
         fill_job(jobs[k], plans[k], desc[pr.a], n[pr.a], pjobs[slot[pr.a]], desc[pr.b], n[pr.b],
@@ -1390,8 +1573,10 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
         serac_zero_counts<<<((int)zero.size() + 255) / 256, 256, 0, stream>>>(dzero, nullptr,
                                                                          (int)zero.size());
     if (e == hipSuccess && nlive) {
+        Clear C = take_clear(w, acc_bytes);
+        C.stride = (uint32_t)prepBlocks * PREP_THREADS;
         serac_prep_many<<<dim3(prepBlocks, (unsigned)prepped.size()), PREP_THREADS, 0, stream>>>(
-            dpjobs, take_clear(w, acc_bytes));
+            dpjobs, C);
         const Gate G = make_gate(d, params);
         hipEvent_t e0, e1;
         prof_slot(e0, e1);
@@ -1433,15 +1618,13 @@ int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int3
         return SERAC_OK;
     const Plan p = make_plan(std::max(nA, 1), std::max(nB, 1), d->cus);
     Workspace *w = nullptr;
-    st = get_workspace(stream, p.acc,
-                       p.scratch + prep_bytes(std::max(nA, 1), true, false) +
-                           prep_bytes(std::max(nB, 1), false, true),
+    st = get_workspace(stream, p.acc, p.scratch + pair_prep_bytes(std::max(nA, 1), std::max(nB, 1)),
                        &w);
     if (st != SERAC_OK)
         return st;
     Job J;
     const PrepJob none{};
-    fill_job(J, p, descA, nA, none, descB, nB, none, w->acc, w->aux, nullptr, nullptr);
+    fill_job(J, p, descA, nA, none, descB, nB, none, next_region(w), w->aux, nullptr, nullptr);
     // with an empty side nothing is raised: rows report (0, -1, 0) and
     // columns (0, -1) from the cleared accumulators
     if (nA > 0 && nB > 0)

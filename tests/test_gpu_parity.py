@@ -132,6 +132,42 @@ def test_zero_and_saturated_rows(serac):
     check_pair(serac, A, B, label="zeros/255")
 
 
+def test_slice_column_ties(serac):
+    """Cross-check ties inside one 16-row slice: a lower row of the slice on
+    the same column with the same best score (duplicate rows), and a lower
+    row whose best is another column but whose second reaches the column
+    maximum, once tying on the column (the match is refused) and once just
+    below it (the match stands)."""
+    rng = np.random.default_rng(21)
+    A = synth.desc(rng, 300) // 4        # low scores everywhere else
+    B = synth.desc(rng, 200) // 4
+    def blk(k, v=255):
+        x = np.zeros(128, np.uint8)
+        x[4 * k:4 * k + 4] = v
+        return x
+    # slice 0: rows 2 and 9 both see column 5 (k = 1) as their only good column
+    B[5] = blk(1)
+    A[2] = blk(1)
+    A[9] = blk(1)
+    # slice 1: row 17 ties columns 7 and 8 (k = 2, 3); row 20 sees column 8
+    B[7] = blk(2)
+    B[8] = blk(3)
+    A[17] = blk(2) | blk(3)
+    A[20] = blk(3)
+    # slice 2: row 33 ties columns 10 and 12 (k = 4, twice) and scores just
+    # below the maximum on column 11 (k = 5); row 40 sees column 11
+    B[10] = blk(4)
+    B[12] = blk(4)
+    B[11] = blk(5)
+    A[33] = blk(4) | blk(5, 254)
+    A[40] = blk(5)
+    got = check_pair(serac, A, B, label="slice column ties")
+    pairs = {tuple(x) for x in got.astype(np.int64).tolist()}
+    assert (2, 5) in pairs and (9, 5) not in pairs
+    assert (20, 8) not in pairs
+    assert (40, 11) in pairs
+
+
 def test_determinism_and_stream(serac):
     p = synth.workload("edge_8192x8192_ties_no255")
     a, b = dev(p.A), dev(p.B)
