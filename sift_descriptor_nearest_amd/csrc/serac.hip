@@ -436,6 +436,17 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
         }
     }
 
+    // ---- column maxima of chunk cc raised into the global column bests,
+    // column k
+    auto flush_col = [&](int cc, int k) {
+        const int col = (c0 + cc) * CHUNK + k;
+        const uint32_t key = sCol[cc * CHUNK + k];
+        if (col < J.nB && (key >> 9) > 0u) {
+            const uint32_t slice = (uint32_t)(rb * (BLOCK_ROWS / SLICE) + 511 - (int)(key & 511u));
+            atomicMax(J.cbest + col, ((unsigned long long)(key >> 9) << 32) | (0xFFFFFFFFu - slice));
+        }
+    };
+
     // ---- chunk staging of prepared sets: 8 + (wave 0) 1 loads per thread
     auto stage = [&](int c, int buf) {
         const uint8_t *src = J.Bp + (size_t)(c0 + c) * CHUNK_BYTES + tid * 16;
@@ -624,19 +635,21 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
               (w & 3) * SCR_WAVE;
     else
         scr = sScr + w * SCR_WAVE;
-    uint32_t *wr = reinterpret_cast<uint32_t *>(scr);
+    // As byte offsets: row 16h + rr, entry n is at wb ^ (264 * rr), and row
+    // n, entry 16h + k at rb ^ (8 * k) (the XOR and the row step touch
+    // disjoint bits), one VALU per access.
+    uint8_t *const sb = reinterpret_cast<uint8_t *>(scr);
+    const uint32_t wb = 4096u * h + 8u * (uint32_t)(n ^ (16 * h));
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-        const int r = 16 * h + rr;                     // row r, entry n
-        wr[2 * (r * 32 + (n ^ r))] = b1[rr];           // two 32-bit stores: no register packing
-        wr[2 * (r * 32 + (n ^ r)) + 1] = b2[rr];
-    }
+    for (int rr = 0; rr < 16; ++rr)
+        *reinterpret_cast<uint2 *>(sb + (wb ^ (264u * rr))) = make_uint2(b1[rr], b2[rr]);
+    const uint32_t rbo = 256u * n + 8u * (uint32_t)((16 * h) ^ n);
     uint32_t K1 = 0u, K2 = 0u;
     int L1 = 64;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         const int src = 16 * h + k;                      // source lane (column)
-        const uint2 e = scr[n * 32 + (src ^ n)];         // row n, entry src
+        const uint2 e = *reinterpret_cast<const uint2 *>(sb + (rbo ^ (8u * k)));   // row n, entry src
         L1 = e.x > K1 ? src : L1;
         K2 = umax3(min(K1, e.x), K2, e.y);
         K1 = max(K1, e.x);
@@ -661,17 +674,8 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
 
     if (COLS) {
         lds_barrier();                       // every wave's column maxima are in
-        const int base = c0 * CHUNK;
-        for (int k = tid; k < nch * CHUNK; k += TILE_THREADS) {
-            const int col = base + k;
-            const uint32_t key = sCol[k];
-            if (col < J.nB && (key >> 9) > 0u) {
-                const uint32_t slice =
-                    (uint32_t)(rb * (BLOCK_ROWS / SLICE) + 511 - (int)(key & 511u));
-                atomicMax(J.cbest + col,
-                          ((unsigned long long)(key >> 9) << 32) | (0xFFFFFFFFu - slice));
-            }
-        }
+        for (int k = tid; k < nch * CHUNK; k += TILE_THREADS)
+            flush_col(k / CHUNK, k % CHUNK);
     }
 }
 

@@ -232,6 +232,55 @@ def test_batch_48x8192(serac):
             assert t <= {tuple(x) for x in want.astype(np.int64).tolist()}
 
 
+# A single pair is swept straight from the raw descriptors up to 2^27
+# products and through the preparation kernel above; both sides of the
+# switch, with ragged tails.
+FUSED_LIMIT = 1 << 27
+
+
+@pytest.mark.parametrize("nA,nB", [(8192, 16384), (8193, 16384), (4096, 32769)],
+                         ids=["8192x16384", "8193x16384", "4096x32769"])
+def test_fused_switch(serac, nA, nB):
+    path = "fused" if nA * nB <= FUSED_LIMIT else "prepared"
+    p = synth.pair(nA, nB, 0.2, 4, seed=nA ^ nB)
+    got = check_pair(serac, p.A, p.B, 0.8, 0.7, True, top2=(nA < 8192),
+                     label=f"switch {nA}x{nB} ({path})")
+    assert len(got) > 0
+
+
+def test_mixed_calls_one_stream(serac):
+    """Fused and prepared sweeps, a batch and a top-2 export in turn on one
+    stream share one workspace; every call starts from clean accumulators."""
+    rng = np.random.default_rng(77)
+    small = synth.pair(700, 900, 0.3, 3, seed=5)
+    big = synth.pair(4096, 32769, 0.2, 4, seed=6)
+    imgs_np = [synth.desc(rng, n) for n in (300, 520, 800)]
+    imgs = [dev(x) for x in imgs_np]
+    pairs = [(0, 1), (1, 2), (2, 0)]
+    want_small = oracle.match_pair(small.A, small.B, 0.8, math.inf, True)
+    want_big = oracle.match_pair(big.A, big.B, 0.8, math.inf, True)
+    want_batch = [oracle.match_pair(imgs_np[a], imgs_np[b], 0.8, math.inf, True)
+                  for a, b in pairs]
+    orow, ocol = oracle.top2(small.A, small.B)
+    sa, sb, ba, bb = dev(small.A), dev(small.B), dev(big.A), dev(big.B)
+    for rep in range(2):
+        say(f"[mixed] round {rep}")
+        got = serac.match_pair(sa, sb).cpu().numpy().astype(np.uint32)
+        assert got.tobytes() == want_small.tobytes(), ("fused", rep)
+        got = serac.match_pair(ba, bb).cpu().numpy().astype(np.uint32)
+        assert got.tobytes() == want_big.tobytes(), ("prepared", rep)
+        res = serac.match_pairs(imgs, pairs)
+        for k in range(len(pairs)):
+            assert res[k].cpu().numpy().astype(np.uint32).tobytes() == want_batch[k].tobytes(), \
+                ("batch", rep, k)
+        row, col = serac.top2(sa, sb)
+        assert_rows_equal(row.cpu().numpy(), orow, f"top2 rows {rep}")
+        assert_rows_equal(col.cpu().numpy(), ocol, f"top2 cols {rep}")
+        got = serac.match_pair(sa, sb, 0.8, math.inf, False).cpu().numpy().astype(np.uint32)
+        assert got.tobytes() == oracle.match_pair(small.A, small.B, 0.8, math.inf,
+                                                  False).tobytes(), ("no cross-check", rep)
+
+
 def test_profiled_launches_exact(serac):
     """Tile launches timed with dispatch-attached events give the same
     results, and the timing is returned for each of them."""
