@@ -120,9 +120,10 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB,
  *   out_matches host array [num_pairs]; out_matches[p] receives pair p's
  *             matches (capacity >= n[pairs[p].a]).
  * Every pair gets exactly the result serac_match_pair would give it.
- * Unlike the other entry points this call returns only after the batch has
- * completed on params->stream (it synchronises that stream), so the host
- * arrays may be released as soon as it returns.
+ * Asynchronous on params->stream like the other entry points: the host
+ * arrays are read before the call returns (they may be released at once);
+ * the library copies what the device needs through pinned memory of its
+ * own.  Results are valid once the stream has synchronised.
  */
 int serac_match_pairs(const uint8_t *const *desc, const int32_t *n,
                       int32_t num_images, const serac_pair *pairs,

@@ -125,7 +125,10 @@ def match_pair(a, b, max_ratio=0.8, max_distance=math.inf, cross_check=True):
     out = torch.empty((max(a.shape[0], 1), 2), dtype=torch.int32, device=a.device)
     count = torch.empty(1, dtype=torch.int32, device=a.device)
     match_pair_into(a, b, out, count, max_ratio, max_distance, cross_check)
-    return out[: int(count.item())]
+    n = int(count.item())
+    if n < 0:
+        raise SeracError(SERAC_ERR_HIP, "serac_match_pair: ordered output hand-off failed")
+    return out[:n]
 
 
 def match_pairs(images, pairs, max_ratio=0.8, max_distance=math.inf,
@@ -139,29 +142,44 @@ def match_pairs(images, pairs, max_ratio=0.8, max_distance=math.inf,
     import torch
     for k, x in enumerate(images):
         _check_desc(x, f"images[{k}]")
-    pairs = [(int(p[0]), int(p[1])) for p in pairs]
-    P = len(pairs)
+    import numpy as np
+    pr = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    P = pr.shape[0]
     if P == 0:
         return []
     dev = images[0].device
-    caps = [max(images[a].shape[0], 1) for a, _ in pairs]
-    offs = [0]
-    for c in caps:
-        offs.append(offs[-1] + c)
-    out = torch.empty((offs[-1], 2), dtype=torch.int32, device=dev)
+    nimg = np.array([x.shape[0] for x in images], dtype=np.int64)
+    if pr.min() < 0 or pr.max() >= len(images):
+        raise SeracError(SERAC_ERR_INVALID_ARG, "serac_match_pairs")
+    caps = np.maximum(nimg[pr[:, 0]], 1)
+    offs = np.zeros(P + 1, dtype=np.int64)
+    np.cumsum(caps, out=offs[1:])
+    out = torch.empty((int(offs[-1]), 2), dtype=torch.int32, device=dev)
     counts = torch.empty(P, dtype=torch.int32, device=dev)
     ptrs = (ctypes.c_void_p * len(images))(*[x.data_ptr() for x in images])
-    ns = (ctypes.c_int32 * len(images))(*[x.shape[0] for x in images])
-    cp = (serac_pair * P)(*[serac_pair(a, b) for a, b in pairs])
-    ms = (serac_matches * P)(*[
-        serac_matches(out.data_ptr() + offs[k] * 8, caps[k], counts.data_ptr() + 4 * k)
-        for k in range(P)])
+    ns = nimg.astype(np.int32)
+    cp = np.ascontiguousarray(pr.astype(np.int32))          # serac_pair [P]
+    ms = np.zeros(P, dtype=[("matches", np.uint64), ("capacity", np.int64),
+                            ("count", np.uint64)])          # serac_matches [P]
+    ms["matches"] = out.data_ptr() + offs[:-1] * 8
+    ms["capacity"] = caps
+    ms["count"] = counts.data_ptr() + 4 * np.arange(P, dtype=np.uint64)
     prm = _params(max_ratio, max_distance, cross_check, _stream(dev))
-    rc = library().serac_match_pairs(ptrs, ns, len(images), cp, P, ctypes.byref(prm), ms)
+    rc = library().serac_match_pairs(ptrs, ns.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                     len(images), cp.ctypes.data_as(ctypes.POINTER(serac_pair)),
+                                     P, ctypes.byref(prm),
+                                     ms.ctypes.data_as(ctypes.POINTER(serac_matches)))
     if rc != SERAC_OK:
         raise SeracError(rc, "serac_match_pairs")
-    cnt = counts.cpu().tolist()
-    return [out[offs[k]: offs[k] + cnt[k]] for k in range(P)]
+    cnt = counts.cpu().numpy().astype(np.int64)
+    if cnt.min() < 0:
+        raise SeracError(SERAC_ERR_HIP, "serac_match_pairs: ordered output hand-off failed")
+    # views of each pair's segment trimmed to its count: one split over
+    # (count, rest) pieces, every other piece kept
+    sizes = np.empty(2 * P, dtype=np.int64)
+    sizes[0::2] = cnt
+    sizes[1::2] = caps - cnt
+    return list(torch.split(out, sizes.tolist())[0::2])
 
 
 def top2(a, b):

@@ -466,10 +466,8 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     wait_vmcnt<0>();                         // chunk 0 and the A operands landed
     if (FUSED) {
         convert(0, 0);
-        if (nch > 1) {
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): raw chunk 0 read back
-            fetch_raw(1);
-        }
+        if (nch > 1)
+            fetch_raw(1);                    // after the read-back (the plane stores use it)
     }
     __syncthreads();
     if (!FUSED && nch > 1)
@@ -574,14 +572,13 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
         frags(buf, 2, 0);
         schedule(Yes{}, Yes{});
         if (FUSED && c + 1 < nch) {
-            // chunk c+1 into the buffer chunk c-1 used; the raw copy of
-            // chunk c+2 follows as soon as this thread's part is read back
+            // chunk c+1 into the buffer chunk c-1 used; then the raw copy of
+            // chunk c+2 (the reads of this thread's part of the raw copy have
+            // returned: the plane stores before it use their data)
             wait_vmcnt<0>();
             convert(c + 1, buf ^ 1);
-            if (c + 2 < nch) {
-                __builtin_amdgcn_s_waitcnt(0xC07F);
+            if (c + 2 < nch)
                 fetch_raw(c + 2);
-            }
             __builtin_amdgcn_sched_barrier(0);
         }
         turn(2);
@@ -1109,7 +1106,10 @@ int device_setup(Device **out)
 //        raised in the other region (which this call does not touch); the
 //        whole buffer is cleared by a kernel when (re)allocated or after a
 //        failed call;
-//   aux  per-call scratch (the job table of a batch, prepared sets).
+//   aux  per-call scratch (the job table of a batch, prepared sets);
+//   stage pinned host memory the job table of a batch is copied from; the
+//        event recorded after that copy tells when it may be rewritten, so
+//        a batch call returns without waiting for its work.
 struct Workspace {
     int dev;
     hipStream_t stream;
@@ -1120,6 +1120,9 @@ struct Workspace {
     uint8_t *aux;
     size_t aux_bytes;
     bool dirty;
+    uint8_t *stage;
+    size_t stage_bytes;
+    hipEvent_t staged;   // recorded after the last copy out of `stage` (or null)
 };
 std::mutex g_ws_mutex;
 std::vector<Workspace> g_ws;
@@ -1160,7 +1163,8 @@ int get_workspace(hipStream_t stream, size_t acc_bytes, size_t aux_bytes, Worksp
         if (e.dev == dev && e.stream == stream)
             w = &e;
     if (!w) {
-        g_ws.push_back(Workspace{dev, stream, nullptr, 0, {0, 0}, 0, nullptr, 0, false});
+        g_ws.push_back(Workspace{dev, stream, nullptr, 0, {0, 0}, 0, nullptr, 0, false, nullptr, 0,
+                                 nullptr});
         w = &g_ws.back();
     }
     const uint8_t *before = w->acc;
@@ -1184,6 +1188,35 @@ int get_workspace(hipStream_t stream, size_t acc_bytes, size_t aux_bytes, Worksp
         st = grow(w->aux, w->aux_bytes, aux_bytes, stream, false);
     *out = w;
     return st;
+}
+
+// Pinned staging memory of at least `bytes`, free to be written (the copy
+// out of it that a previous call enqueued has run).
+int get_stage(Workspace *w, size_t bytes, uint8_t **out)
+{
+    if (w->staged && hipEventSynchronize(w->staged) != hipSuccess)
+        return hip_fail();
+    if (w->stage_bytes < bytes) {
+        if (w->stage)
+            (void)hipHostFree(w->stage);
+        w->stage = nullptr;
+        w->stage_bytes = 0;
+        const size_t want = std::max(align256(bytes), (size_t)1 << 20);
+        if (hipHostMalloc(reinterpret_cast<void **>(&w->stage), want, hipHostMallocDefault) !=
+            hipSuccess) {
+            (void)hipGetLastError();
+            w->stage = nullptr;
+            return SERAC_ERR_OUT_OF_MEMORY;
+        }
+        w->stage_bytes = want;
+    }
+    if (!w->staged &&
+        hipEventCreateWithFlags(&w->staged, hipEventDisableTiming) != hipSuccess) {
+        w->staged = nullptr;
+        return hip_fail();
+    }
+    *out = w->stage;
+    return SERAC_OK;
 }
 
 // The accumulator region of the next call (zero).
@@ -1540,15 +1573,19 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
     const size_t jobs_bytes = align256(sizeof(Job) * (size_t)std::max(nlive, 1));
     const size_t prepjobs_bytes = align256(sizeof(PrepJob) * std::max<size_t>(prepped.size(), 1));
     const size_t zero_bytes = align256(sizeof(int32_t *) * zero.size() + 8);
-    std::vector<uint8_t> host(jobs_bytes + prepjobs_bytes + zero_bytes);
+    const size_t host_bytes = jobs_bytes + prepjobs_bytes + zero_bytes;
     Workspace *w = nullptr;
-    st = get_workspace(stream, acc_bytes, host.size() + res_bytes + prep_total, &w);
+    st = get_workspace(stream, acc_bytes, host_bytes + res_bytes + prep_total, &w);
     if (st != SERAC_OK)
         return st;
-    Job *jobs = reinterpret_cast<Job *>(host.data());
-    PrepJob *pjobs = reinterpret_cast<PrepJob *>(host.data() + jobs_bytes);
-    int32_t **zp = reinterpret_cast<int32_t **>(host.data() + jobs_bytes + prepjobs_bytes);
-    uint8_t *rq = w->aux + host.size();
+    uint8_t *host = nullptr;
+    st = get_stage(w, host_bytes, &host);
+    if (st != SERAC_OK)
+        return st;
+    Job *jobs = reinterpret_cast<Job *>(host);
+    PrepJob *pjobs = reinterpret_cast<PrepJob *>(host + jobs_bytes);
+    int32_t **zp = reinterpret_cast<int32_t **>(host + jobs_bytes + prepjobs_bytes);
+    uint8_t *rq = w->aux + host_bytes;
     uint8_t *pq = rq + res_bytes;
     std::vector<int> slot(num_images, -1);
     int prepBlocks = 1;
@@ -1568,7 +1605,9 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
     }
     for (size_t k = 0; k < zero.size(); ++k)
         zp[k] = zero[k];
-    hipError_t e = hipMemcpyAsync(w->aux, host.data(), host.size(), hipMemcpyHostToDevice, stream);
+    hipError_t e = hipMemcpyAsync(w->aux, host, host_bytes, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess)
+        e = hipEventRecord(w->staged, stream);   // `stage` is reusable once this has run
     const Job *djobs = reinterpret_cast<const Job *>(w->aux);
     const PrepJob *dpjobs = reinterpret_cast<const PrepJob *>(w->aux + jobs_bytes);
     int32_t *const *dzero =
@@ -1596,10 +1635,6 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
     }
     if (e == hipSuccess)
         e = hipGetLastError();
-    if (e == hipSuccess) {
-        // the staging buffer `host` must outlive the copy
-        e = hipStreamSynchronize(stream);
-    }
     if (e != hipSuccess) {
         mark_dirty(w);
         return hip_fail();
