@@ -616,6 +616,13 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
         chunk(c);
 
     __builtin_amdgcn_s_setprio(0);
+    // ---- column maxima out first: their atomics complete behind the merge
+    if (COLS) {
+        lds_barrier();                       // every wave's column maxima are in
+        for (int k = tid; k < nch * CHUNK; k += TILE_THREADS)
+            flush_col(k / CHUNK, k % CHUNK);
+    }
+
     // ---- merge the 32 lanes that share each row, through this wave's own
     // LDS scratch (no barrier: only this wave writes and reads it): lane pair
     // (q, q + 32) folds the entries of source lanes 0..15 and 16..31 of row
@@ -669,11 +676,6 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
         J.rslot[(size_t)cg * J.nA + row] = pack_slot(S1, col, S2);
     }
 
-    if (COLS) {
-        lds_barrier();                       // every wave's column maxima are in
-        for (int k = tid; k < nch * CHUNK; k += TILE_THREADS)
-            flush_col(k / CHUNK, k % CHUNK);
-    }
 }
 
 template <bool COLS>
