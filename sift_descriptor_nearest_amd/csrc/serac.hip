@@ -82,8 +82,9 @@ constexpr int SLICE = 16;               // rows per column tie-break slice
 constexpr int CHUNK = 256;              // columns of B per LDS chunk
 constexpr int CHUNK_BYTES = CHUNK * DIM;
 constexpr int PLANE_BYTES = CHUNK * 16; // one 16-byte part of every column
-constexpr int GROUP_MAX = 2048;         // columns per workgroup: 64 tiles (6-bit index)
+constexpr int GROUP_MAX = 16384;        // columns per workgroup: 512 tiles (the keys' 9-bit index)
 constexpr int MAX_GCH = GROUP_MAX / CHUNK;
+constexpr int COL_RING = 8;             // chunks of column maxima a workgroup keeps in LDS
 constexpr int SCR_WAVE = WAVE_ROWS * 32;  // lane-merge scratch entries per wave (32 rows x 32)
 constexpr int PREP_THREADS = 256;
 constexpr int NORM2 = 262144;           // 512^2
@@ -99,7 +100,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 //   RT  [rowsA] row term 128*SA - 2^21.
 //   Bp  [rowsB/256][8 parts][256 columns][16 B]: part p of column j holds
 //       bytes [16*p, +16) of that descriptor, ^ 0x80.
-//   P   [rowsB] key addend ((128*SB) << 9) + (511 - ((j >> 5) & 63)).
+//   P   [rowsB] key addend ((128*SB) << 9) + (511 - ((j >> 5) & 511)).
 // Rows beyond n are all-zero descriptors: their score against anything is 0.
 struct PrepJob {
     const uint8_t *X;
@@ -268,7 +269,7 @@ __device__ __forceinline__ void prep_body(const PrepJob &Q, int blk)
         const size_t off = (((size_t)c * 8 + part) * CHUNK + j) * 16;
         *reinterpret_cast<uint4 *>(Q.Bp + off) = x;
         if (part == 0)
-            Q.P[r] = ((128u * s) << 9) + (uint32_t)(511 - ((r >> 5) & 63));
+            Q.P[r] = ((128u * s) << 9) + (uint32_t)(511 - ((r >> 5) & 511));
     }
 }
 
@@ -332,7 +333,7 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     // chunk buffers (operand planes), and for a fused sweep the raw chunk
     __shared__ __attribute__((aligned(16))) uint8_t sB[(FUSED ? 3 : 2) * CHUNK_BYTES];
     __shared__ __attribute__((aligned(16))) uint32_t sP[2 * CHUNK];
-    __shared__ uint32_t sCol[COLS ? GROUP_MAX : 1];
+    __shared__ uint32_t sCol[COLS ? COL_RING * CHUNK : 1];   // ring of chunks: chunk c at c % 8
     // lane-merge scratch, 8 KiB per wave; a fused sweep merges in the LDS
     // its chunks no longer use
     __shared__ uint2 sScr[FUSED ? 1 : TILE_WAVES * SCR_WAVE];
@@ -381,7 +382,7 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
         sum += (uint32_t)__builtin_amdgcn_mov_dpp((int)sum, 0xB1, 0xF, 0xF, false);
         const int col = (c0 + c) * CHUNK + hcol;
         if (hf == 0)
-            sP[buf * CHUNK + hcol] = ((128u * sum) << 9) + (uint32_t)(511 - ((col >> 5) & 63));
+            sP[buf * CHUNK + hcol] = ((128u * sum) << 9) + (uint32_t)(511 - ((col >> 5) & 511));
     };
 
     // ---- this wave's rows of A: operand fragments and the row terms
@@ -440,7 +441,7 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     // column k
     auto flush_col = [&](int cc, int k) {
         const int col = (c0 + cc) * CHUNK + k;
-        const uint32_t key = sCol[cc * CHUNK + k];
+        const uint32_t key = sCol[(cc & (COL_RING - 1)) * CHUNK + k];
         if (col < J.nB && (key >> 9) > 0u) {
             const uint32_t slice = (uint32_t)(rb * (BLOCK_ROWS / SLICE) + 511 - (int)(key & 511u));
             atomicMax(J.cbest + col, ((unsigned long long)(key >> 9) << 32) | (0xFFFFFFFFu - slice));
@@ -460,7 +461,7 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     if (!FUSED)
         stage(0, 0);
     if (COLS) {
-        for (int k = tid; k < nch * CHUNK; k += TILE_THREADS)
+        for (int k = tid; k < min(nch, COL_RING) * CHUNK; k += TILE_THREADS)
             sCol[k] = 0u;
     }
     wait_vmcnt<0>();                         // chunk 0 and the A operands landed
@@ -529,7 +530,7 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
             }
             const uint32_t cm0 = max(umax3(m0[0], m0[1], m0[2]), umax3(m0[3], m0[4], k0[15]));
             const uint32_t cm1 = max(umax3(m1[0], m1[1], m1[2]), umax3(m1[3], m1[4], k1[15]));
-            uint32_t *cp = sCol + c * CHUNK + pr * 64 + n;
+            uint32_t *cp = sCol + (c & (COL_RING - 1)) * CHUNK + pr * 64 + n;
             atomicMax(cp, (cm0 & ~511u) | tag);
             atomicMax(cp + 32, (cm1 & ~511u) | tag);
         }
@@ -581,6 +582,15 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
                 fetch_raw(c + 2);
             __builtin_amdgcn_sched_barrier(0);
         }
+        if (COLS && c >= COL_RING - 1) {
+            // chunk c-7's column maxima are final (every wave is past two
+            // chunk barriers since); its ring slot is chunk c+1's
+            if (tid < CHUNK) {
+                flush_col(c - (COL_RING - 1), tid);
+                sCol[((c + 1) & (COL_RING - 1)) * CHUNK + tid] = 0u;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         turn(2);
         mfma(0);
         epi(1, c, 1, Odd{});
@@ -619,7 +629,9 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     // ---- column maxima out first: their atomics complete behind the merge
     if (COLS) {
         lds_barrier();                       // every wave's column maxima are in
-        for (int k = tid; k < nch * CHUNK; k += TILE_THREADS)
+        // the chunks still in the ring
+        for (int k = max(nch - (COL_RING - 1), 0) * CHUNK + tid; k < nch * CHUNK;
+             k += TILE_THREADS)
             flush_col(k / CHUNK, k % CHUNK);
     }
 

@@ -248,6 +248,14 @@ def test_fused_switch(serac, nA, nB):
     assert len(got) > 0
 
 
+def test_wide_column_groups(serac):
+    """A tall pair gets 64-chunk (16384-column) column groups: column maxima
+    leave the 8-chunk LDS ring during the sweep, tile tags use all 9 bits,
+    and the last group is a single ragged chunk."""
+    p = synth.pair(65536, 16384 + 100, 0.05, 3, seed=65)
+    check_pair(serac, p.A, p.B, 0.8, 0.7, True, top2=True, label="wide groups 65536x16484")
+
+
 def test_mixed_calls_one_stream(serac):
     """Fused and prepared sweeps, a batch and a top-2 export in turn on one
     stream share one workspace; every call starts from clean accumulators."""
