@@ -65,6 +65,7 @@
 #include <cstdint>
 #include <cstring>
 #include <algorithm>
+#include <deque>
 #include <mutex>
 #include <type_traits>
 #include <vector>
@@ -1139,7 +1140,7 @@ struct Workspace {
     hipEvent_t staged;   // recorded after the last copy out of `stage` (or null)
 };
 std::mutex g_ws_mutex;
-std::vector<Workspace> g_ws;
+std::deque<Workspace> g_ws;     // a deque: workspaces keep their addresses as others are added
 
 int grow(uint8_t *&ptr, size_t &have, size_t need, hipStream_t stream, bool clear)
 {

@@ -289,6 +289,40 @@ def test_mixed_calls_one_stream(serac):
                                                   False).tobytes(), ("no cross-check", rep)
 
 
+def test_two_streams(serac):
+    """Calls on two streams interleave (one workspace per stream); from two
+    host threads as well."""
+    import threading
+    p1 = synth.pair(1500, 1300, 0.3, 3, seed=31)
+    p2 = synth.pair(900, 2500, 0.3, 3, seed=32)
+    want = [oracle.match_pair(p.A, p.B, 0.8, math.inf, True) for p in (p1, p2)]
+    dv = [(dev(p.A), dev(p.B)) for p in (p1, p2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[None] * 4 for _ in range(2)]
+
+    def run(k, reps):
+        with torch.cuda.stream(streams[k]):
+            a, b = dv[k]
+            for r in range(reps):
+                out = torch.full((a.shape[0], 2), -1, dtype=torch.int32, device="cuda:0")
+                cnt = torch.full((1,), -7, dtype=torch.int32, device="cuda:0")
+                serac.match_pair_into(a, b, out, cnt)
+                outs[k][r] = (out, cnt)
+    for r in range(4):                       # interleaved on one host thread
+        run(0, 1) if r % 2 == 0 else run(1, 1)
+    torch.cuda.synchronize()
+    th = [threading.Thread(target=run, args=(k, 4)) for k in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    torch.cuda.synchronize()
+    for k in range(2):
+        for out, cnt in outs[k]:
+            n = int(cnt.item())
+            assert out[:n].cpu().numpy().astype(np.uint32).tobytes() == want[k].tobytes(), k
+
+
 def test_profiled_launches_exact(serac):
     """Tile launches timed with dispatch-attached events give the same
     results, and the timing is returned for each of them."""
