@@ -92,8 +92,8 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE {world}); pairs are independent, see DESIGN.md for how "
-              "the path would shard", file=sys.stderr)
+              f"WORLD_SIZE {world}); pairs are independent, so several GPUs would "
+              "each match their own share of the pair list", file=sys.stderr)
         return 2
 
     import numpy as np
