@@ -82,8 +82,10 @@ typedef struct serac_match {
  * ascending order of a; count: device int32 receiving the number written,
  * or -1 if the device-side ordering hand-off between workgroups did not
  * complete (a bounded wait that only a malfunctioning device exhausts; the
- * match list is then invalid).  capacity must be at least nA (each row
- * yields at most one match). */
+ * match list is then invalid).  The bound is 2^22 polls; for tests, the
+ * environment variable SERAC_LOOKBACK_SPIN_LIMIT read at the first call on
+ * a device replaces it (-1: give up at once).  capacity must be at least nA
+ * (each row yields at most one match). */
 typedef struct serac_matches {
     serac_match *matches;
     int64_t capacity;

@@ -63,6 +63,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <algorithm>
 #include <deque>
@@ -154,6 +155,7 @@ struct Gate {
     double max_ratio;
     double max_distance;
     int32_t cross_check;
+    int32_t spin_limit;      // look-back polls before giving up (< 0: give up at once)
 };
 
 // A row's result over one column group packed into 64 bits, ordered like
@@ -797,7 +799,7 @@ __device__ __forceinline__ void slice_ties(uint32_t S1, uint32_t S2, int32_t I1,
 constexpr unsigned long long ST_OWN = 1ull << 62;        // own match count published
 constexpr unsigned long long ST_INCL = 2ull << 62;       // inclusive prefix published
 constexpr unsigned long long ST_ERR = 3ull << 62;        // look-back gave up
-constexpr int FINISH_SPIN_LIMIT = 1 << 22;
+constexpr int FINISH_SPIN_LIMIT = 1 << 22;   // default look-back polls
 
 __device__ __forceinline__ unsigned long long status_load(unsigned long long *p)
 {
@@ -889,7 +891,8 @@ __device__ __forceinline__ void finish_body(const Job &J, int wg, int nwg, const
             if (lane == 0)
                 status_store(st + wg, ST_OWN | (unsigned)tot);
             int k0 = wg - 1, spins = 0;
-            for (;;) {
+            failed = G.spin_limit < 0;
+            while (!failed) {
                 const int k = k0 - lane;
                 // before group 0 there is an inclusive prefix of 0
                 const unsigned long long v = k >= 0 ? status_load(st + k) : ST_INCL;
@@ -902,7 +905,7 @@ __device__ __forceinline__ void finish_body(const Job &J, int wg, int nwg, const
                     break;
                 }
                 if (__ballot(state == 0ull) & upto) {
-                    if (++spins > FINISH_SPIN_LIMIT) {
+                    if (++spins > G.spin_limit) {
                         failed = true;
                         break;
                     }
@@ -1023,6 +1026,7 @@ struct Device {
     int status = SERAC_OK;
     int cus = 0;
     double *table = nullptr;
+    int spin_limit = FINISH_SPIN_LIMIT;
 };
 
 std::mutex g_mutex;
@@ -1085,6 +1089,14 @@ int device_setup(Device **out)
             return d.status;
         }
         d.cus = prop.multiProcessorCount;
+        // test hook: SERAC_LOOKBACK_SPIN_LIMIT bounds the finishing kernel's
+        // look-back polls (negative: give up at once, so count = -1)
+        if (const char *e = std::getenv("SERAC_LOOKBACK_SPIN_LIMIT")) {
+            char *end = nullptr;
+            const long v = std::strtol(e, &end, 10);
+            if (end != e && v >= -1 && v <= (1L << 30))
+                d.spin_limit = (int)v;
+        }
         // angle of every attainable clamped score, with the C library's acos
         std::vector<double> t(NORM2 + 1);
         for (int s = 0; s <= NORM2; ++s)
@@ -1386,6 +1398,7 @@ Gate make_gate(const Device *d, const serac_params *p)
     G.max_ratio = p->max_ratio;
     G.max_distance = p->max_distance;
     G.cross_check = p->cross_check;
+    G.spin_limit = d->spin_limit;
     return G;
 }
 

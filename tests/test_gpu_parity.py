@@ -323,6 +323,38 @@ def test_two_streams(serac):
             assert out[:n].cpu().numpy().astype(np.uint32).tobytes() == want[k].tobytes(), k
 
 
+def test_lookback_failure_reported():
+    """The finishing kernel's bounded look-back: with the host forcing it to
+    give up at once (SERAC_LOOKBACK_SPIN_LIMIT=-1, read at the first call),
+    the count is -1 and the binding raises; every kernel still exits
+    normally.  Its own process, so the setting stays out of the others."""
+    import os
+    import subprocess
+    code = (
+        "import sys, torch, numpy as np\n"
+        "sys.path.insert(0, %r)\n"
+        "import sift_descriptor_nearest_amd as serac\n"
+        "from sift_descriptor_nearest_amd import synth\n"
+        "p = synth.pair(700, 500, 0.3, 3, seed=3)\n"
+        "a = torch.from_numpy(p.A).cuda(); b = torch.from_numpy(p.B).cuda()\n"
+        "out = torch.empty((700, 2), dtype=torch.int32, device='cuda')\n"
+        "cnt = torch.full((1,), 7, dtype=torch.int32, device='cuda')\n"
+        "serac.match_pair_into(a, b, out, cnt)\n"
+        "print('count', int(cnt.item()), flush=True)\n"
+        "try:\n"
+        "    serac.match_pair(a, b)\n"
+        "    print('no error', flush=True)\n"
+        "except serac.SeracError as e:\n"
+        "    print('raised', e, flush=True)\n"
+    ) % (str(__import__('pathlib').Path(__file__).resolve().parents[1]),)
+    env = dict(os.environ, SERAC_LOOKBACK_SPIN_LIMIT="-1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       timeout=180)
+    say(r.stdout.strip())
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "count -1" in r.stdout and "raised" in r.stdout, r.stdout
+
+
 def test_profiled_launches_exact(serac):
     """Tile launches timed with dispatch-attached events give the same
     results, and the timing is returned for each of them."""
