@@ -552,9 +552,7 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
 
     // Steps do not mix: each step's MFMAs, epilogue and operand reads are
     // scheduled among themselves.
-    auto schedule = [&](auto, auto) { __builtin_amdgcn_sched_barrier(0); };
-    using Yes = std::integral_constant<bool, true>;
-    using No = std::integral_constant<bool, false>;
+    auto step_end = [&]() { __builtin_amdgcn_sched_barrier(0); };
 
     // chunk c: pairs 1..3 of the chunk and pair 0 of the next one (pair 0
     // of chunk 0 is issued before the loop)
@@ -574,7 +572,7 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
         mfma(1);
         epi(0, c, 0, Even{});
         frags(buf, 2, 0);
-        schedule(Yes{}, Yes{});
+        step_end();
         if (FUSED && c + 1 < nch) {
             // chunk c+1 into the buffer chunk c-1 used; then the raw copy of
             // chunk c+2 (the reads of this thread's part of the raw copy have
@@ -598,11 +596,11 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
         mfma(0);
         epi(1, c, 1, Odd{});
         frags(buf, 3, 1);
-        schedule(Yes{}, Yes{});
+        step_end();
         turn(3);
         mfma(1);
         epi(0, c, 2, Even{});
-        schedule(Yes{}, No{});
+        step_end();
         if (c + 1 < nch) {
             if (!FUSED)
                 wait_vmcnt<0>();             // chunk c+1 landed (this wave's part)
@@ -615,7 +613,7 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
             mfma(0);
             epi(1, c, 3, Odd{});
             frags(buf ^ 1, 1, 1);
-            schedule(Yes{}, Yes{});
+            step_end();
         } else {
             epi(1, c, 3, Odd{});
         }
@@ -624,7 +622,7 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     frags(0, 0, 0);
     mfma(0);
     frags(0, 1, 1);
-    schedule(No{}, Yes{});
+    step_end();
     for (int c = 0; c < nch; ++c)
         chunk(c);
 
@@ -682,7 +680,8 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
         K1 = max(K1, o1);
     }
     // publish this row block's top-2 over the workgroup's columns as one
-    // packed slot per (row, column group); the gate merges the groups
+    // packed slot per (row, column group); the finishing kernel merges the
+    // groups
     const int row = rb * BLOCK_ROWS + w * WAVE_ROWS + n;
     if (h == 0 && row < J.nA) {
         const uint32_t S1 = K1 >> 9, S2 = K2 >> 9;
@@ -795,7 +794,7 @@ __device__ __forceinline__ void slice_ties(uint32_t S1, uint32_t S2, int32_t I1,
 }
 
 // Cross-workgroup hand-off of the finishing kernel: one 64-bit status word
-// per gate workgroup, bits 63..62 the state and bits 31..0 a count.
+// per finishing workgroup, bits 63..62 the state and bits 31..0 a count.
 constexpr unsigned long long ST_OWN = 1ull << 62;        // own match count published
 constexpr unsigned long long ST_INCL = 2ull << 62;       // inclusive prefix published
 constexpr unsigned long long ST_ERR = 3ull << 62;        // look-back gave up
