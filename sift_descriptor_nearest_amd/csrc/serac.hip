@@ -18,14 +18,16 @@
 //     every term exact in int32 (|sum a'b'| <= 2^21, S < 2^23).
 //     The row term 128*SA_i - 2^21 enters through the MFMA accumulator input,
 //     so it costs no vector instruction.
-//   * A preparation kernel converts each set once per call into the layouts
-//     the tile kernel reads: A as per-lane MFMA operand fragments plus the
-//     row terms, B as 256-column chunks of eight 16-byte "planes" plus each
-//     column's key addend.  The tile kernel then streams B chunks straight
-//     from global memory into LDS (global_load_lds_dwordx4: no registers,
-//     no vector instructions), fetching chunk c+1 into the second buffer
-//     while chunk c is swept.
-//   * A workgroup is eight waves, two per SIMD, 256 rows of A by up to 2048
+//   * The tile kernel reads A as per-lane MFMA operand fragments plus the
+//     row terms, and B as 256-column chunks of eight 16-byte "planes" plus
+//     each column's key addend, double-buffered in LDS.  For one pair up to
+//     2^27 products it builds these itself from the raw descriptors: A in
+//     its prologue, each B chunk copied raw into LDS (global_load_lds) and
+//     converted during the chunk before.  Larger pairs and batches get a
+//     preparation kernel that converts each set once; the tile kernel then
+//     streams the prepared chunks straight into LDS (no registers, no
+//     vector instructions).
+//   * A workgroup is eight waves, two per SIMD, 256 rows of A by up to 16384
 //     columns of B, one workgroup per CU: the eight waves share every staged
 //     B chunk and the per-chunk barrier keeps them in step (two smaller
 //     workgroups on one CU drift apart, the older one taking the issue
@@ -36,7 +38,7 @@
 //     matrix core and the vector ALU work side by side.
 //   * Each score becomes one packed 32-bit key
 //       key = (S << 9) | (511 - t),
-//     t being the index of its 32-column tile in the 2048-column window, in
+//     t being the index of its 32-column tile in the 16384-column window, in
 //     one v_lshl_add (the column term 128*SB_j is folded into the addend).
 //     A key comparison orders by score, then by lowest column.  Scores stay
 //     below 2^23, so the key is exact.
@@ -48,9 +50,11 @@
 //   * Column best: a max3 tree over the 16 rows a lane holds in one tile
 //     gives the column maximum of those rows; the key's low 9 bits are then
 //     replaced by the 16-row slice number (lowest slice wins) and merged with
-//     an LDS atomic max.  The exact lowest row inside the winning slice is
-//     settled afterwards from the 15 rows that precede it (rarely more than
-//     a filter check).
+//     an LDS atomic max into a ring of eight chunks, which goes out to the
+//     global column bests (64-bit atomic max) during the sweep.  The exact
+//     lowest row inside the winning slice is settled afterwards from the 15
+//     rows that precede it, compared in registers (an exact product only in
+//     the rare case the bounds leave open).
 //   * All merges (across lanes, waves, workgroups) compare packed keys or
 //     scan in ascending index order, so the result does not depend on
 //     scheduling (MASDA part 3, section 6: an order-independent key).
