@@ -150,7 +150,9 @@ int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB,
  * in `every` (the first, then every `every`-th) made by serac_match_pair,
  * serac_match_pairs or serac_top2_pair is dispatched with hipExtLaunchKernel
  * carrying one pair as its start and stop events, recorded by the dispatch
- * itself on the call's stream.  The event handling slows the enqueueing
+ * itself on the call's stream.  The events carry no system-scope fence, so a
+ * timed dispatch ends like an untimed one (a default event would add a cache
+ * write-back for the host to it).  The event handling slows the enqueueing
  * host; timing a fraction of the launches keeps the queue as full as
  * without it.  serac_profile_stop waits for the recorded events, returns
  * the summed device time in milliseconds and the number of launches timed,

@@ -560,12 +560,15 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
 
     // chunk c: pairs 1..3 of the chunk and pair 0 of the next one (pair 0
     // of chunk 0 is issued before the loop)
-    // The two waves of a SIMD take turns at the higher issue priority, one
-    // step each, so that neither runs ahead (with equal priorities the older
-    // wave is always issued first and the other finishes every chunk alone).
+    // Issue priority of the two waves sharing a SIMD: with equal priorities
+    // the older wave is always issued first and the other finishes every
+    // chunk alone.  The younger wave takes the higher priority in steps 0..2
+    // (and the conversion after step 1), the older one in step 3; with this
+    // split both arrive at the chunk barrier about together (measured: an
+    // even split still left the younger wave ~0.5 us behind per chunk).
     const bool second = (w >> 2) & 1;        // waves w and w + 4 share a SIMD
     auto turn = [&](int k) {
-        if (((k & 1) != 0) == second)
+        if ((k != 3) == second)
             __builtin_amdgcn_s_setprio(1);
         else
             __builtin_amdgcn_s_setprio(0);
@@ -1725,8 +1728,11 @@ int serac_profile_start(int32_t max_launches, int32_t every)
     g_prof.seen = 0;
     g_prof.every = every;
     g_prof.armed = false;
+    // Without a system-scope fence: a default event makes its dispatch
+    // write the caches back for the host at the end, which lengthened the
+    // timed launches by ~1.3 us against the untimed ones (profiler trace).
     for (auto &e : g_prof.ev) {
-        if (hipEventCreate(&e) != hipSuccess) {
+        if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
             e = nullptr;
             return hip_fail();
         }
