@@ -19,6 +19,9 @@ HIPCC_FLAGS = [
     # register-allocation inconsistency fails the build instead of producing
     # a kernel that computes wrong results
     "-mllvm", "-verify-machineinstrs",
+    # pass the first 16 dwords of scalar kernel arguments in SGPRs at wave
+    # launch (kernels whose first loads depend on them take them first)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

@@ -638,9 +638,10 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     if (COLS) {
         lds_barrier();                       // every wave's column maxima are in
         // the chunks still in the ring
-        for (int k = max(nch - (COL_RING - 1), 0) * CHUNK + tid; k < nch * CHUNK;
-             k += TILE_THREADS)
-            flush_col(k / CHUNK, k % CHUNK);
+#pragma unroll 2
+        for (uint32_t k = (uint32_t)(max(nch - (COL_RING - 1), 0) * CHUNK + tid);
+             k < (uint32_t)(nch * CHUNK); k += TILE_THREADS)
+            flush_col((int)(k / CHUNK), (int)(k % CHUNK));
     }
 
     // ---- merge the 32 lanes that share each row, through this wave's own
@@ -669,15 +670,15 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
         *reinterpret_cast<uint2 *>(sb + (wb ^ (264u * rr))) = make_uint2(b1[rr], b2[rr]);
     const uint32_t rbo = 256u * n + 8u * (uint32_t)((16 * h) ^ n);
     uint32_t K1 = 0u, K2 = 0u;
-    int L1 = 64;
+    int k1 = 0;                                          // K1 came from source lane 16h + k1
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-        const int src = 16 * h + k;                      // source lane (column)
-        const uint2 e = *reinterpret_cast<const uint2 *>(sb + (rbo ^ (8u * k)));   // row n, entry src
-        L1 = e.x > K1 ? src : L1;
+        const uint2 e = *reinterpret_cast<const uint2 *>(sb + (rbo ^ (8u * k)));   // row n, entry 16h + k
+        k1 = e.x > K1 ? k : k1;
         K2 = umax3(min(K1, e.x), K2, e.y);
         K1 = max(K1, e.x);
     }
+    int L1 = 16 * h + k1;                                // source lane (column in the tile)
     {
         // lane half 0 holds the lower source lanes: it keeps its own on a tie
         const uint32_t o1 = __shfl_xor(K1, 32), o2 = __shfl_xor(K2, 32);
@@ -708,10 +709,25 @@ __global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_one(Job J)
 // One pair straight from the raw descriptors (no preparation kernel); also
 // clears what the previous call on the stream left raised (the other
 // accumulator region, which this call does not touch).
+//
+// The fields the sweep needs first are also passed as leading scalar
+// arguments: the build preloads the first 16 argument dwords into SGPRs at
+// wave launch, while a struct argument is read from the argument buffer in
+// memory before the first load can be addressed.  They override the copies
+// in J.
 template <bool COLS>
-__global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_fused(Job J, Clear C)
+__global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_fused(
+    const uint8_t *A, const uint8_t *B, int32_t nA, int32_t nB, int32_t nRB, int32_t nBC,
+    int32_t gch, uint4 *clear_p, uint32_t clear_words, uint32_t clear_stride, Job J)
 {
-    clear_body<TILE_THREADS>(C);
+    J.A = A;
+    J.B = B;
+    J.nA = nA;
+    J.nB = nB;
+    J.nRB = nRB;
+    J.nBC = nBC;
+    J.gch = gch;
+    clear_body<TILE_THREADS>(Clear{clear_p, clear_words, clear_stride});
     tiles_body<COLS, true>(J, blockIdx.x);
 }
 
@@ -946,8 +962,19 @@ __device__ __forceinline__ void finish_body(const Job &J, int wg, int nwg, const
     }
 }
 
-__global__ __launch_bounds__(GATE_THREADS) void serac_finish_one(Job J, Gate G)
+// The fields read first as leading scalar arguments (preloaded into SGPRs,
+// like the fused sweep's); they override the copies in J and G.
+__global__ __launch_bounds__(GATE_THREADS) void serac_finish_one(
+    const unsigned long long *rslot, int32_t nA, int32_t nB, int32_t Gc,
+    unsigned long long *cbest, const double *table, int32_t cross_check, Job J, Gate G)
 {
+    J.rslot = const_cast<unsigned long long *>(rslot);
+    J.nA = nA;
+    J.nB = nB;
+    J.Gc = Gc;
+    J.cbest = cbest;
+    G.table = table;
+    G.cross_check = cross_check;
     finish_body(J, blockIdx.x, (J.nA + GATE_THREADS - 1) / GATE_THREADS, G);
 }
 
@@ -1442,6 +1469,20 @@ size_t pair_prep_bytes(int nA, int nB)
     return fused_pair(nA, nB) ? 0 : prep_bytes(nA, true, false) + prep_bytes(nB, false, true);
 }
 
+// The fused sweep, with the timing events e0/e1 attached when not null.
+template <bool COLS>
+void launch_fused(const Job &J, uint4 *clear_p, uint32_t clear_words, uint32_t clear_stride,
+                  int units, hipStream_t stream, hipEvent_t e0, hipEvent_t e1)
+{
+    if (e0)
+        hipExtLaunchKernelGGL(serac_tiles_fused<COLS>, dim3(units), dim3(TILE_THREADS), 0, stream,
+                              e0, e1, 0, J.A, J.B, J.nA, J.nB, J.nRB, J.nBC, J.gch, clear_p,
+                              clear_words, clear_stride, J);
+    else
+        serac_tiles_fused<COLS><<<units, TILE_THREADS, 0, stream>>>(
+            J.A, J.B, J.nA, J.nB, J.nRB, J.nBC, J.gch, clear_p, clear_words, clear_stride, J);
+}
+
 // Preparation and tile sweep of one pair (nA, nB > 0) on `stream`; the
 // prepared sets go to `prep` (pair_prep_bytes(nA, nB)).
 void launch_pair(Job &J, const Plan &p, const uint8_t *A, int nA, const uint8_t *B, int nB,
@@ -1451,18 +1492,13 @@ void launch_pair(Job &J, const Plan &p, const uint8_t *A, int nA, const uint8_t 
         C.stride = (uint32_t)p.units() * TILE_THREADS;
         hipEvent_t e0, e1;
         prof_slot(e0, e1);
-        if (e0) {
-            if (cols)
-                hipExtLaunchKernelGGL(serac_tiles_fused<true>, dim3(p.units()),
-                                      dim3(TILE_THREADS), 0, stream, e0, e1, 0, J, C);
-            else
-                hipExtLaunchKernelGGL(serac_tiles_fused<false>, dim3(p.units()),
-                                      dim3(TILE_THREADS), 0, stream, e0, e1, 0, J, C);
-        } else if (cols) {
-            serac_tiles_fused<true><<<p.units(), TILE_THREADS, 0, stream>>>(J, C);
-        } else {
-            serac_tiles_fused<false><<<p.units(), TILE_THREADS, 0, stream>>>(J, C);
-        }
+        // (the cleared region is a few MiB at most: its 16-byte word count
+        // fits 32 bits)
+        const uint32_t words = (uint32_t)C.words;
+        if (cols)
+            launch_fused<true>(J, C.p, words, C.stride, p.units(), stream, e0, e1);
+        else
+            launch_fused<false>(J, C.p, words, C.stride, p.units(), stream, e0, e1);
         return;
     }
     uint8_t *q = prep;
@@ -1532,7 +1568,8 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int
     launch_pair(J, p, descA, nA, descB, nB, w->aux + p.scratch, take_clear(w, p.acc),
                 params->cross_check != 0, stream);
     const Gate G = make_gate(d, params);
-    serac_finish_one<<<(nA + GATE_THREADS - 1) / GATE_THREADS, GATE_THREADS, 0, stream>>>(J, G);
+    serac_finish_one<<<(nA + GATE_THREADS - 1) / GATE_THREADS, GATE_THREADS, 0, stream>>>(
+        J.rslot, J.nA, J.nB, J.Gc, J.cbest, G.table, G.cross_check, J, G);
     if (hipGetLastError() != hipSuccess) {
         mark_dirty(w);
         return SERAC_ERR_HIP;
