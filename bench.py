@@ -41,13 +41,17 @@ KERNEL_SRC = os.path.join(ROOT, "sift_descriptor_nearest_amd", "csrc", "serac.hi
 
 
 def kernel_sha() -> str:
+    """sha256 of the kernel source and the compiler flags it is built with."""
+    from sift_descriptor_nearest_amd.build import HIPCC_FLAGS
     with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+        src = f.read()
+    return hashlib.sha256(src + b"\0" + " ".join(HIPCC_FLAGS).encode()).hexdigest()
 
 
 def measured_traffic():
     """HBM bytes per tile-kernel launch from committed counter runs, or None
-    when the kernel source has changed since they were taken."""
+    when the kernel source or its build flags have changed since they were
+    taken."""
     try:
         with open(TRAFFIC) as f:
             t = json.load(f)
