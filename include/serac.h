@@ -28,6 +28,9 @@
  *     pool on that stream and returned on it.
  *   - Results are deterministic: they do not depend on occupancy, launch
  *     order or the number of compute units.
+ *   - Calls may come from several host threads.  Calls on one stream share
+ *     that stream's device workspace and are serialized by the library;
+ *     their order on the stream is the order in which they acquire it.
  *   - Arguments are validated before any HIP call; on an error nothing is
  *     enqueued and no output is written.
  *   - Only gfx950 devices are supported; any other device is refused with

@@ -1158,8 +1158,10 @@ int device_setup(Device **out)
 
 // Grow-only workspace per (device, stream).  Work on one stream runs in
 // order, so consecutive calls on a stream can share one workspace; calls on
-// different streams get different ones.  Growth frees the old buffers and
-// allocates new ones on the same stream, both stream-ordered.
+// different streams get different ones.  A call holds its workspace's lock
+// while it enqueues, so calls on one stream from several host threads are
+// serialized (their enqueue order is their stream order).  Growth frees the
+// old buffers and allocates new ones on the same stream, both stream-ordered.
 //   acc  the accumulators of the jobs, in two equal regions that calls use
 //        in turn; a call's region is zero when it starts: the first kernel
 //        of each call clears the leading bytes the previous call left
@@ -1171,20 +1173,21 @@ int device_setup(Device **out)
 //        event recorded after that copy tells when it may be rewritten, so
 //        a batch call returns without waiting for its work.
 struct Workspace {
-    int dev;
-    hipStream_t stream;
-    uint8_t *acc;
-    size_t acc_bytes;    // both regions
-    size_t acc_used[2];  // leading bytes of each region the last call on it left raised
-    int region;          // the region the next call uses (zero)
-    uint8_t *aux;
-    size_t aux_bytes;
-    bool dirty;
-    uint8_t *stage;
-    size_t stage_bytes;
-    hipEvent_t staged;   // recorded after the last copy out of `stage` (or null)
+    int dev = 0;
+    hipStream_t stream = nullptr;
+    uint8_t *acc = nullptr;
+    size_t acc_bytes = 0;            // both regions
+    size_t acc_used[2] = {0, 0};     // leading bytes of each region the last call on it left raised
+    int region = 0;                  // the region the next call uses (zero)
+    uint8_t *aux = nullptr;
+    size_t aux_bytes = 0;
+    bool dirty = false;
+    uint8_t *stage = nullptr;
+    size_t stage_bytes = 0;
+    hipEvent_t staged = nullptr;     // recorded after the last copy out of `stage` (or null)
+    std::mutex busy;                 // held by the call enqueueing on this workspace
 };
-std::mutex g_ws_mutex;
+std::mutex g_ws_mutex;          // guards the list itself
 std::deque<Workspace> g_ws;     // a deque: workspaces keep their addresses as others are added
 
 int grow(uint8_t *&ptr, size_t &have, size_t need, hipStream_t stream, bool clear)
@@ -1211,22 +1214,27 @@ int grow(uint8_t *&ptr, size_t &have, size_t need, hipStream_t stream, bool clea
 }
 
 // The workspace of the current device and `stream`, with at least the
-// given sizes; returns it locked to the caller's use via *out.
-int get_workspace(hipStream_t stream, size_t acc_bytes, size_t aux_bytes, Workspace **out)
+// given sizes, in *out; `hold` receives its lock, which the caller keeps
+// until it has enqueued its work (also when this returns an error).
+int get_workspace(hipStream_t stream, size_t acc_bytes, size_t aux_bytes, Workspace **out,
+                  std::unique_lock<std::mutex> &hold)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return hip_fail();
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace *w = nullptr;
-    for (auto &e : g_ws)
-        if (e.dev == dev && e.stream == stream)
-            w = &e;
-    if (!w) {
-        g_ws.push_back(Workspace{dev, stream, nullptr, 0, {0, 0}, 0, nullptr, 0, false, nullptr, 0,
-                                 nullptr});
-        w = &g_ws.back();
+    {
+        std::lock_guard<std::mutex> lock(g_ws_mutex);
+        for (auto &e : g_ws)
+            if (e.dev == dev && e.stream == stream)
+                w = &e;
+        if (!w) {
+            w = &g_ws.emplace_back();
+            w->dev = dev;
+            w->stream = stream;
+        }
     }
+    hold = std::unique_lock<std::mutex>(w->busy);
     const uint8_t *before = w->acc;
     // two regions of at least acc_bytes each (grow's minimum keeps halves
     // 256-byte aligned)
@@ -1279,10 +1287,10 @@ int get_stage(Workspace *w, size_t bytes, uint8_t **out)
     return SERAC_OK;
 }
 
-// The accumulator region of the next call (zero).
+// The accumulator region of the next call (zero).  (This and the two below
+// run under the workspace's lock.)
 uint8_t *next_region(Workspace *w)
 {
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
     return w->acc + (size_t)w->region * (w->acc_bytes / 2);
 }
 
@@ -1291,7 +1299,6 @@ uint8_t *next_region(Workspace *w)
 // records what this call will leave in its own.
 Clear take_clear(Workspace *w, size_t leaves)
 {
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
     const int cur = w->region, other = 1 - cur;
     Clear C;
     C.stride = 1;                            // set by the launch
@@ -1307,7 +1314,6 @@ Clear take_clear(Workspace *w, size_t leaves)
 // left them raised: have the next call clear them first.
 void mark_dirty(Workspace *w)
 {
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
     w->dirty = true;
 }
 
@@ -1558,7 +1564,8 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int
     }
     const Plan p = make_plan(nA, nB, d->cus);
     Workspace *w = nullptr;
-    st = get_workspace(stream, p.acc, p.scratch + pair_prep_bytes(nA, nB), &w);
+    std::unique_lock<std::mutex> hold;
+    st = get_workspace(stream, p.acc, p.scratch + pair_prep_bytes(nA, nB), &w, hold);
     if (st != SERAC_OK)
         return st;
     Job J;
@@ -1646,7 +1653,8 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
     const size_t zero_bytes = align256(sizeof(int32_t *) * zero.size() + 8);
     const size_t host_bytes = jobs_bytes + prepjobs_bytes + zero_bytes;
     Workspace *w = nullptr;
-    st = get_workspace(stream, acc_bytes, host_bytes + res_bytes + prep_total, &w);
+    std::unique_lock<std::mutex> hold;
+    st = get_workspace(stream, acc_bytes, host_bytes + res_bytes + prep_total, &w, hold);
     if (st != SERAC_OK)
         return st;
     uint8_t *host = nullptr;
@@ -1728,8 +1736,9 @@ int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int3
         return SERAC_OK;
     const Plan p = make_plan(std::max(nA, 1), std::max(nB, 1), d->cus);
     Workspace *w = nullptr;
+    std::unique_lock<std::mutex> hold;
     st = get_workspace(stream, p.acc, p.scratch + pair_prep_bytes(std::max(nA, 1), std::max(nB, 1)),
-                       &w);
+                       &w, hold);
     if (st != SERAC_OK)
         return st;
     Job J;

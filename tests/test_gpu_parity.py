@@ -323,6 +323,40 @@ def test_two_streams(serac):
             assert out[:n].cpu().numpy().astype(np.uint32).tobytes() == want[k].tobytes(), k
 
 
+def test_threads_one_stream(serac):
+    """Two host threads calling on the same stream share its workspace; the
+    library serializes their enqueues, also while one of them grows it (a
+    fused pair and a larger prepared pair in turn)."""
+    import threading
+    p1 = synth.pair(1500, 1300, 0.3, 3, seed=41)
+    p2 = synth.pair(2600, 52000, 0.2, 3, seed=42)       # above 2^27 products: prepared
+    want = [oracle.match_pair(p.A, p.B, 0.8, math.inf, True) for p in (p1, p2)]
+    dv = [(dev(p.A), dev(p.B)) for p in (p1, p2)]
+    stream = torch.cuda.Stream()
+    reps = 6
+    outs = [[None] * reps for _ in range(2)]
+
+    def run(k):
+        with torch.cuda.stream(stream):
+            a, b = dv[k]
+            for r in range(reps):
+                out = torch.full((a.shape[0], 2), -1, dtype=torch.int32, device="cuda:0")
+                cnt = torch.full((1,), -7, dtype=torch.int32, device="cuda:0")
+                serac.match_pair_into(a, b, out, cnt)
+                outs[k][r] = (out, cnt)
+    say("[threads] two host threads, one stream")
+    th = [threading.Thread(target=run, args=(k,)) for k in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    torch.cuda.synchronize()
+    for k in range(2):
+        for r, (out, cnt) in enumerate(outs[k]):
+            n = int(cnt.item())
+            assert out[:n].cpu().numpy().astype(np.uint32).tobytes() == want[k].tobytes(), (k, r)
+
+
 def test_lookback_failure_reported():
     """The finishing kernel's bounded look-back: with the host forcing it to
     give up at once (SERAC_LOOKBACK_SPIN_LIMIT=-1, read at the first call),
