@@ -88,6 +88,45 @@ def test_planted_pairs(serac, nA, nB):
     assert len(got) > 0
 
 
+def _random_case(k):
+    """Case k of the seeded sweep: a shape near a tile boundary or arbitrary,
+    one of four generators, and one setting of the gates."""
+    rng = np.random.default_rng(10_000 + k)
+
+    def size(hi):
+        if rng.random() < 0.5:                   # next to a 32-, 256- or 512-multiple
+            m = int(rng.choice([32, 256, 512]))
+            return int(max(1, m * rng.integers(1, hi // m + 1) + rng.integers(-1, 2)))
+        return int(rng.integers(1, hi + 1))
+    nA, nB = size(2600), size(4700)
+    kind = ("planted", "tie", "random", "coarse")[k % 4]
+    if kind == "planted":
+        p = synth.pair(nA, nB, 0.3, 3, seed=k)
+        A, B = p.A, p.B
+    elif kind == "tie":
+        A, B = tie_heavy(rng, nA), tie_heavy(rng, nB)
+    elif kind == "random":
+        A, B = synth.desc(rng, nA), synth.desc(rng, nB)
+    else:                                        # bytes 0 or 45: scores are multiples of 2025
+        A = (rng.integers(0, 2, (nA, 128)) * 45).astype(np.uint8)
+        B = (rng.integers(0, 2, (nB, 128)) * 45).astype(np.uint8)
+    if kind in ("tie", "coarse"):                # lenient gates, so that tied bests can pass
+        ratio = float(rng.choice([1.0, 1.3]))
+        dist = math.inf if kind == "tie" else float(rng.choice([math.inf, 1.2]))
+    else:
+        ratio = float(rng.choice([0.6, 0.8, 1.0, 1.3]))
+        dist = float(rng.choice([math.inf, 0.3, 0.7]))
+    cross = bool(rng.random() < 0.7)
+    return kind, A, B, ratio, dist, cross
+
+
+@pytest.mark.parametrize("k", range(40))
+def test_random_sweep(serac, k):
+    kind, A, B, ratio, dist, cross = _random_case(k)
+    check_pair(serac, A, B, ratio, dist, cross, top2=(k % 3 == 0),
+               label=f"sweep {k} {kind}")
+
+
 def test_workload_pair_1000x1200(serac):
     p = synth.workload("pair_1000x1200")
     got = check_pair(serac, p.A, p.B, **p.params(), label=p.name)
