@@ -91,7 +91,12 @@ constexpr int PLANE_BYTES = CHUNK * 16; // one 16-byte part of every column
 constexpr int GROUP_MAX = 16384;        // columns per workgroup: 512 tiles (the keys' 9-bit index)
 constexpr int MAX_GCH = GROUP_MAX / CHUNK;
 constexpr int COL_RING = 8;             // chunks of column maxima a workgroup keeps in LDS
-constexpr int SCR_WAVE = WAVE_ROWS * 32;  // lane-merge scratch entries per wave (32 rows x 32)
+constexpr int SCR_ROW = 33;              // lane-merge scratch: 32 entries per row plus one of padding
+constexpr int SCR_WAVE = WAVE_ROWS * SCR_ROW;   // entries per wave (8448 bytes)
+// LDS chunk buffer stride: a chunk plus 1 KiB, so that a buffer the chunks no
+// longer use holds the lane-merge scratch of four waves
+constexpr int BUF_BYTES = CHUNK_BYTES + 1024;
+static_assert(4 * SCR_WAVE * 8 <= BUF_BYTES, "merge scratch of four waves in one chunk buffer");
 constexpr int PREP_THREADS = 256;
 constexpr int NORM2 = 262144;           // 512^2
 constexpr int GATE_THREADS = 256;
@@ -338,14 +343,14 @@ template <bool COLS, bool FUSED>
 __device__ __forceinline__ void tiles_body(const Job &J, int u)
 {
     // chunk buffers (operand planes), and for a fused sweep the raw chunk
-    __shared__ __attribute__((aligned(16))) uint8_t sB[(FUSED ? 3 : 2) * CHUNK_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[(FUSED ? 3 : 2) * BUF_BYTES];
     __shared__ __attribute__((aligned(16))) uint32_t sP[2 * CHUNK];
     __shared__ uint32_t sCol[COLS ? COL_RING * CHUNK : 1];   // ring of chunks: chunk c at c % 8
     // lane-merge scratch, 8 KiB per wave; a fused sweep merges in the LDS
     // its chunks no longer use
     __shared__ uint2 sScr[FUSED ? 1 : TILE_WAVES * SCR_WAVE];
     __shared__ __attribute__((aligned(16))) int32_t sRT[FUSED ? BLOCK_ROWS : 1];
-    uint8_t *const sRaw = sB + 2 * CHUNK_BYTES;
+    uint8_t *const sRaw = sB + 2 * BUF_BYTES;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -381,7 +386,7 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
             sum += bytesum16(v[k]);
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            *reinterpret_cast<uint4 *>(sB + buf * CHUNK_BYTES + (4 * hf + k) * PLANE_BYTES +
+            *reinterpret_cast<uint4 *>(sB + buf * BUF_BYTES + (4 * hf + k) * PLANE_BYTES +
                                        hcol * 16) =
                 make_uint4(v[k].x ^ 0x80808080u, v[k].y ^ 0x80808080u, v[k].z ^ 0x80808080u,
                            v[k].w ^ 0x80808080u);
@@ -458,7 +463,7 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     // ---- chunk staging of prepared sets: 8 + (wave 0) 1 loads per thread
     auto stage = [&](int c, int buf) {
         const uint8_t *src = J.Bp + (size_t)(c0 + c) * CHUNK_BYTES + tid * 16;
-        uint8_t *dst = sB + buf * CHUNK_BYTES + w * 1024;
+        uint8_t *dst = sB + buf * BUF_BYTES + w * 1024;
 #pragma unroll
         for (int k = 0; k < CHUNK_BYTES / (TILE_THREADS * 16); ++k)
             load_lds16(src + k * (TILE_THREADS * 16), dst + k * (TILE_THREADS * 16));
@@ -500,7 +505,7 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     const uint32_t tag = (uint32_t)(511 - (2 * w + h));
 
     auto frags = [&](int buf, int pr, int set) {
-        const uint8_t *base = sB + buf * CHUNK_BYTES + h * PLANE_BYTES + n * 16 + pr * 1024;
+        const uint8_t *base = sB + buf * BUF_BYTES + h * PLANE_BYTES + n * 16 + pr * 1024;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
@@ -649,31 +654,30 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     // (q, q + 32) folds the entries of source lanes 0..15 and 16..31 of row
     // q in ascending order, so on a key tie (same score, same tile) the
     // first, lowest lane, which is the lowest column, stays.
-    // Entry e of row r sits at r*32 + (e ^ r): the stores of one row and the
-    // loads of one entry from 32 rows both fall on distinct banks.  A fused
-    // sweep uses the 64 KiB its chunks left free (every wave is past the last
-    // chunk barrier): the buffer of chunk nch-2 for waves 0..3, the raw copy
-    // for waves 4..7.
+    // Entry e of row r sits at 33*r + e (rows padded by one entry): the
+    // stores of one row and the loads of one entry from 32 rows both fall on
+    // distinct banks, and every access is a fixed offset from a per-lane
+    // base.  A fused sweep uses the buffers its chunks left free (every wave
+    // is past the last chunk barrier): the buffer of chunk nch-2 for waves
+    // 0..3, the raw copy for waves 4..7.
     uint2 *scr;
     if (FUSED)
-        scr = reinterpret_cast<uint2 *>((w < 4 ? sB + (nch & 1) * CHUNK_BYTES : sRaw)) +
+        scr = reinterpret_cast<uint2 *>((w < 4 ? sB + (nch & 1) * BUF_BYTES : sRaw)) +
               (w & 3) * SCR_WAVE;
     else
         scr = sScr + w * SCR_WAVE;
-    // As byte offsets: row 16h + rr, entry n is at wb ^ (264 * rr), and row
-    // n, entry 16h + k at rb ^ (8 * k) (the XOR and the row step touch
-    // disjoint bits), one VALU per access.
-    uint8_t *const sb = reinterpret_cast<uint8_t *>(scr);
-    const uint32_t wb = 4096u * h + 8u * (uint32_t)(n ^ (16 * h));
+    // Row 16h + rr, entry n is at wb + SCR_ROW*rr, and row n, entry 16h + k
+    // at rb + k.
+    uint2 *const wb = scr + SCR_ROW * 16 * h + n;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr)
-        *reinterpret_cast<uint2 *>(sb + (wb ^ (264u * rr))) = make_uint2(b1[rr], b2[rr]);
-    const uint32_t rbo = 256u * n + 8u * (uint32_t)((16 * h) ^ n);
+        wb[SCR_ROW * rr] = make_uint2(b1[rr], b2[rr]);
+    const uint2 *const rbp = scr + SCR_ROW * n + 16 * h;
     uint32_t K1 = 0u, K2 = 0u;
     int k1 = 0;                                          // K1 came from source lane 16h + k1
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-        const uint2 e = *reinterpret_cast<const uint2 *>(sb + (rbo ^ (8u * k)));   // row n, entry 16h + k
+        const uint2 e = rbp[k];                          // row n, entry 16h + k
         k1 = e.x > K1 ? k : k1;
         K2 = umax3(min(K1, e.x), K2, e.y);
         K1 = max(K1, e.x);
