@@ -70,7 +70,7 @@ def cpu_baseline(p, budget_s: float):
         ref = oracle.match_pair(p.A, p.B, **p.params())
         runs += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or runs >= 50:
+        if el >= budget_s or runs >= 200:
             break
     return ref, {"value": round(ops * runs / el / 1e12, 4), "unit": "TOPS",
                  "cores": oracle.max_threads(), "kind": "oracle",
