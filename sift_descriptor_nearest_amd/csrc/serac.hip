@@ -346,7 +346,7 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     __shared__ __attribute__((aligned(16))) uint8_t sB[(FUSED ? 3 : 2) * BUF_BYTES];
     __shared__ __attribute__((aligned(16))) uint32_t sP[2 * CHUNK];
     __shared__ uint32_t sCol[COLS ? COL_RING * CHUNK : 1];   // ring of chunks: chunk c at c % 8
-    // lane-merge scratch, 8 KiB per wave; a fused sweep merges in the LDS
+    // lane-merge scratch, 8448 bytes per wave; a fused sweep merges in the LDS
     // its chunks no longer use
     __shared__ uint2 sScr[FUSED ? 1 : TILE_WAVES * SCR_WAVE];
     __shared__ __attribute__((aligned(16))) int32_t sRT[FUSED ? BLOCK_ROWS : 1];
