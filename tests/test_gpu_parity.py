@@ -250,6 +250,36 @@ def test_workload_pair_32768_sampled(serac):
     assert {tuple(x) for x in p.truth.tolist()} <= {tuple(x) for x in got.tolist()}
 
 
+def test_max_size_sampled(serac):
+    """The largest accepted set (SERAC_MAX_DESCRIPTORS = 262144 rows of A)
+    against 262143 rows of B (16 column groups of 16384 columns, a ragged
+    last chunk, 1024 finishing workgroups): sampled rows and columns against
+    the oracle, whole-list properties at full size."""
+    say("[parity] max size: generating 262144 x 262143")
+    p = synth.pair(262144, 262143, 0.02, 3, seed=262)
+    a, b = dev(p.A), dev(p.B)
+    say("[parity] max size: GPU match and top-2 export")
+    got = serac.match_pair(a, b, 0.8, math.inf, True).cpu().numpy().astype(np.int64)
+    row, col = serac.top2(a, b)
+    row, col = row.cpu().numpy(), col.cpu().numpy()
+    rng = np.random.default_rng(12)
+    sample = np.unique(np.concatenate([rng.choice(len(p.A), 96, replace=False),
+                                       p.truth[:32, 0], [0, len(p.A) - 1]])).astype(np.int32)
+    say(f"[parity] max size: oracle on {len(sample)} sampled rows")
+    dec = oracle.match_rows(p.A, p.B, sample, 0.8, math.inf, True)
+    gmap = {int(x[0]): int(x[1]) for x in got}
+    for i in sample.tolist():
+        assert gmap.get(i, -1) == dec[i], i
+    assert np.array_equal(row[sample], oracle.rows(p.A, p.B, sample))
+    csample = np.unique(np.concatenate([rng.choice(len(p.B), 96, replace=False),
+                                        p.truth[:32, 1], [len(p.B) - 1]])).astype(np.int32)
+    assert np.array_equal(col[csample], oracle.cols(p.A, p.B, csample))
+    assert np.all(np.diff(got[:, 0]) > 0)
+    assert len(np.unique(got[:, 1])) == len(got)
+    assert np.all(row[got[:, 0], 1] == got[:, 1]) and np.all(col[got[:, 1], 1] == got[:, 0])
+    assert {tuple(x) for x in p.truth.tolist()} <= {tuple(x) for x in got.tolist()}
+
+
 def test_batch_48x8192(serac):
     bt = synth.exhaustive_48x8192()
     imgs = [dev(x) for x in bt.images]
