@@ -150,7 +150,7 @@ struct Job {
     const uint32_t *P;
     int32_t nA, nB;
     int32_t nRB, nBC;        // 128-row blocks of A, 256-column chunks of B
-    int32_t gch, Gc;         // chunks per workgroup (1, 2, 4 or 8), column groups
+    int32_t gch, Gc;         // chunks per workgroup (a power of two up to 64), column groups
     unsigned long long *rslot;  // [Gc][nA] one row result per column group (see pack_slot)
     uint32_t *rs1;              // [nA] best score per row (column export scratch)
     unsigned long long *cbest;  // [nB] (best << 32) | ~slice    (max: lowest slice)
@@ -1329,8 +1329,15 @@ struct Plan {
 };
 
 // Workgroups of 256 rows by gch chunks of 256 columns; gch (a power of two,
-// at most 8, so a workgroup's columns stay inside one aligned 2048-column
+// at most 64, so a workgroup's columns stay inside one aligned 16384-column
 // window) is the largest that still yields about `target` workgroups.
+//
+// Workgroup u sweeps row block u % nRB against column group u / nRB.
+// Consecutive workgroups go to the eight XCDs in turn, so with nRB a
+// multiple of 8 all sweeps of a row block share one XCD, and so does the
+// finishing workgroup of that row block (256 rows each).  Every XCD's L2
+// then fetches all of B; a map giving each XCD a 2-D block of the grid cut
+// the fetched bytes by a third but made both kernels slower (measured).
 Plan make_plan(int nA, int nB, long long target)
 {
     Plan p;
