@@ -918,6 +918,12 @@ __device__ __forceinline__ void finish_body(const Job &J, int wg, int nwg, const
                 status_store(st + wg, ST_OWN | (unsigned)tot);
             int k0 = wg - 1, spins = 0;
             failed = G.spin_limit < 0;
+            // The groups publish within ~0.4 us of each other, and a poll
+            // that finds a predecessor still unpublished costs a whole
+            // round trip: waiting ~0.4 us first (12 x 64 clocks) lets most
+            // look-backs end with their first poll (measured: -0.45 us per
+            // 8192 x 8192 call; 32 finishing groups).
+            __builtin_amdgcn_s_sleep(12);
             while (!failed) {
                 const int k = k0 - lane;
                 // before group 0 there is an inclusive prefix of 0
