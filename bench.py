@@ -172,7 +172,7 @@ def main() -> int:
                      "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                      "frac": round(achieved / PEAK_INT8_TOPS, 4),
                      "traffic": measured_traffic(),
-                     "kernel": "serac_tiles_fused<true>",
+                     "kernel": "serac_tiles_fused<true, true>",
                      "kernel_us": round(k_s * 1e6, 3), "launches": launches},
         "matches": int(len(got)),
     }

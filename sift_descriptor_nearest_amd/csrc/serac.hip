@@ -153,7 +153,8 @@ struct Job {
     int32_t gch, Gc;         // chunks per workgroup (a power of two up to 64), column groups
     unsigned long long *rslot;  // [Gc][nA] one row result per column group (see pack_slot)
     uint32_t *rs1;              // [nA] best score per row (column export scratch)
-    unsigned long long *cbest;  // [nB] (best << 32) | ~slice    (max: lowest slice)
+    unsigned long long *cbest;  // [nB] column bests (see col_best_at), raised by atomic maxima
+    int32_t cb32;            // 1: 32-bit column bests (at most 512 slices, nA <= 8192)
     unsigned long long *status;  // [ceil(nA / 256)] finishing hand-off (zero before the finish)
     serac_match *out;        // [>= nA]
     int32_t *count;          // 1
@@ -183,6 +184,26 @@ __host__ __device__ __forceinline__ unsigned long long pack_slot(uint32_t S1, ui
         return 0ull;
     return ((unsigned long long)S1 << 41) |
            ((unsigned long long)(SLOT_COL_MAX - col) << 23) | (unsigned long long)S2;
+}
+
+// A column's best: its score and the 16-row slice holding the first row
+// that reaches it (lowest slice on a tie), raised by atomic maxima.  With at
+// most 512 slices (nA <= 8192) it takes 32 bits, (S << 9) | (511 - slice);
+// otherwise 64, (S << 32) | ~slice.  Both order by score, then lowest
+// slice, and are 0 for a column no row scores above 0 on.  The 64-bit
+// atomic maximum costs ~0.6 us more per 8192 x 8192 sweep than the 32-bit
+// one (measured), hence the narrow form where it fits.
+__device__ __forceinline__ void col_best_at(const Job &J, int j, uint32_t &C1, int32_t &slice)
+{
+    if (J.cb32) {
+        const uint32_t v = reinterpret_cast<const uint32_t *>(J.cbest)[j];
+        C1 = v >> 9;
+        slice = 511 - (int32_t)(v & 511u);
+    } else {
+        const unsigned long long v = J.cbest[j];
+        C1 = (uint32_t)(v >> 32);
+        slice = (int32_t)(0xFFFFFFFFu - (uint32_t)v);
+    }
 }
 
 // 128 zero bytes: the descriptor a fused sweep reads for columns past the end
@@ -339,7 +360,7 @@ __global__ __launch_bounds__(PREP_THREADS) void serac_prep_many(const PrepJob *_
 // terms in the prologue, and each chunk of B in two stages, a copy of the
 // raw chunk into LDS and, during the chunk before the one that needs it,
 // its conversion into the operand planes and the columns' key addends.
-template <bool COLS, bool FUSED>
+template <bool COLS, bool FUSED, bool NARROW>
 __device__ __forceinline__ void tiles_body(const Job &J, int u)
 {
     // chunk buffers (operand planes), and for a fused sweep the raw chunk
@@ -456,7 +477,11 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
         const uint32_t key = sCol[(cc & (COL_RING - 1)) * CHUNK + k];
         if (col < J.nB && (key >> 9) > 0u) {
             const uint32_t slice = (uint32_t)(rb * (BLOCK_ROWS / SLICE) + 511 - (int)(key & 511u));
-            atomicMax(J.cbest + col, ((unsigned long long)(key >> 9) << 32) | (0xFFFFFFFFu - slice));
+            if constexpr (NARROW)
+                atomicMax(reinterpret_cast<uint32_t *>(J.cbest) + col, (key & ~511u) | (511u - slice));
+            else
+                atomicMax(J.cbest + col,
+                          ((unsigned long long)(key >> 9) << 32) | (0xFFFFFFFFu - slice));
         }
     };
 
@@ -704,10 +729,11 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
 
 }
 
-template <bool COLS>
+// NARROW: the column bests take 32 bits (J.cb32; see col_best_at).
+template <bool COLS, bool NARROW>
 __global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_one(Job J)
 {
-    tiles_body<COLS, false>(J, blockIdx.x);
+    tiles_body<COLS, false, NARROW>(J, blockIdx.x);
 }
 
 // One pair straight from the raw descriptors (no preparation kernel); also
@@ -719,7 +745,7 @@ __global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_one(Job J)
 // wave launch, while a struct argument is read from the argument buffer in
 // memory before the first load can be addressed.  They override the copies
 // in J.
-template <bool COLS>
+template <bool COLS, bool NARROW>
 __global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_fused(
     const uint8_t *A, const uint8_t *B, int32_t nA, int32_t nB, int32_t nRB, int32_t nBC,
     int32_t gch, uint4 *clear_p, uint32_t clear_words, uint32_t clear_stride, Job J)
@@ -732,10 +758,10 @@ __global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_fused(
     J.nBC = nBC;
     J.gch = gch;
     clear_body<TILE_THREADS>(Clear{clear_p, clear_words, clear_stride});
-    tiles_body<COLS, true>(J, blockIdx.x);
+    tiles_body<COLS, true, NARROW>(J, blockIdx.x);
 }
 
-template <bool COLS>
+template <bool COLS, bool NARROW>
 __global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_many(const Job *__restrict__ jobs,
                                                                     int unitsPerJob)
 {
@@ -743,7 +769,7 @@ __global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_many(const Job *_
     const int u = blockIdx.x % unitsPerJob;
     if (u >= J.nRB * J.Gc)
         return;
-    tiles_body<COLS, false>(J, u);
+    tiles_body<COLS, false, NARROW>(J, u);
 }
 
 // Exact inner product of two descriptors (used only to settle column ties
@@ -860,17 +886,16 @@ __device__ __forceinline__ void finish_body(const Job &J, int wg, int nwg, const
         row_result(J, i, S1, I1, S2);
     const bool cand = I1 >= 0 && I1 < J.nB;
     double d1 = 0.0, d2 = 0.0;
-    unsigned long long cb = 0ull;
+    uint32_t C1 = 0u;
+    int32_t slice = -1;
     if (cand) {
         d1 = G.table[min(S1, (uint32_t)NORM2)];
         d2 = G.table[min(S2, (uint32_t)NORM2)];
         if (G.cross_check)
-            cb = J.cbest[I1];
+            col_best_at(J, I1, C1, slice);
     }
     bool acc = cand && (d1 <= G.max_distance) && (d1 < G.max_ratio * d2);
     if (G.cross_check) {
-        const uint32_t C1 = (uint32_t)(cb >> 32);
-        const int32_t slice = (int32_t)(0xFFFFFFFFu - (uint32_t)cb);
         acc = acc && C1 == S1 && slice == i / SLICE;
         // Row i is its column's best only if no lower row of its 16-row
         // slice (the lanes below it in its 16-lane row) reaches C1 on that
@@ -1043,9 +1068,9 @@ __global__ void serac_export_cols(Job J, int32_t *col_best)
     const int j = blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= J.nB)
         return;
-    const unsigned long long key = J.cbest[j];
-    const uint32_t C1 = (uint32_t)(key >> 32);
-    const int32_t slice = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
+    uint32_t C1;
+    int32_t slice;
+    col_best_at(J, j, C1, slice);
     int32_t idx = -1;
     if (C1 > 0u) {
         const uint8_t *b = J.B + (size_t)j * DIM;
@@ -1058,7 +1083,10 @@ __global__ void serac_export_cols(Job J, int32_t *col_best)
     }
     col_best[2 * (size_t)j] = (int32_t)C1;
     col_best[2 * (size_t)j + 1] = idx;
-    J.cbest[j] = 0ull;
+    if (J.cb32)
+        reinterpret_cast<uint32_t *>(J.cbest)[j] = 0u;
+    else
+        J.cbest[j] = 0ull;
 }
 
 
@@ -1421,6 +1449,7 @@ void fill_job(Job &J, const Plan &p, const uint8_t *A, int nA, const PrepJob &QA
     J.nBC = p.nBC;
     J.gch = p.gch;
     J.Gc = p.Gc;
+    J.cb32 = p.nRB * (BLOCK_ROWS / SLICE) <= 512 ? 1 : 0;
     J.cbest = reinterpret_cast<unsigned long long *>(acc);
     J.status = reinterpret_cast<unsigned long long *>(acc + align256((size_t)nB * 8));
     J.rs1 = reinterpret_cast<uint32_t *>(scratch);
@@ -1458,22 +1487,26 @@ Gate make_gate(const Device *d, const serac_params *p)
     return G;
 }
 
+template <bool COLS, bool NARROW>
+void launch_one(const Job &J, int units, hipStream_t stream, hipEvent_t e0, hipEvent_t e1)
+{
+    if (e0)
+        hipExtLaunchKernelGGL(serac_tiles_one<COLS, NARROW>, dim3(units), dim3(TILE_THREADS), 0,
+                              stream, e0, e1, 0, J);
+    else
+        serac_tiles_one<COLS, NARROW><<<units, TILE_THREADS, 0, stream>>>(J);
+}
+
 void launch_tiles(const Job &J, const Plan &p, bool cols, hipStream_t stream)
 {
     hipEvent_t e0, e1;
     prof_slot(e0, e1);
-    if (e0) {
-        if (cols)
-            hipExtLaunchKernelGGL(serac_tiles_one<true>, dim3(p.units()), dim3(TILE_THREADS), 0,
-                                  stream, e0, e1, 0, J);
-        else
-            hipExtLaunchKernelGGL(serac_tiles_one<false>, dim3(p.units()), dim3(TILE_THREADS), 0,
-                                  stream, e0, e1, 0, J);
-    } else if (cols) {
-        serac_tiles_one<true><<<p.units(), TILE_THREADS, 0, stream>>>(J);
-    } else {
-        serac_tiles_one<false><<<p.units(), TILE_THREADS, 0, stream>>>(J);
-    }
+    if (!cols)
+        launch_one<false, false>(J, p.units(), stream, e0, e1);
+    else if (J.cb32)
+        launch_one<true, true>(J, p.units(), stream, e0, e1);
+    else
+        launch_one<true, false>(J, p.units(), stream, e0, e1);
 }
 
 // A pair small enough that converting the raw descriptors inside the sweep
@@ -1493,16 +1526,16 @@ size_t pair_prep_bytes(int nA, int nB)
 }
 
 // The fused sweep, with the timing events e0/e1 attached when not null.
-template <bool COLS>
+template <bool COLS, bool NARROW>
 void launch_fused(const Job &J, uint4 *clear_p, uint32_t clear_words, uint32_t clear_stride,
                   int units, hipStream_t stream, hipEvent_t e0, hipEvent_t e1)
 {
     if (e0)
-        hipExtLaunchKernelGGL(serac_tiles_fused<COLS>, dim3(units), dim3(TILE_THREADS), 0, stream,
-                              e0, e1, 0, J.A, J.B, J.nA, J.nB, J.nRB, J.nBC, J.gch, clear_p,
-                              clear_words, clear_stride, J);
+        hipExtLaunchKernelGGL(serac_tiles_fused<COLS, NARROW>, dim3(units), dim3(TILE_THREADS), 0,
+                              stream, e0, e1, 0, J.A, J.B, J.nA, J.nB, J.nRB, J.nBC, J.gch,
+                              clear_p, clear_words, clear_stride, J);
     else
-        serac_tiles_fused<COLS><<<units, TILE_THREADS, 0, stream>>>(
+        serac_tiles_fused<COLS, NARROW><<<units, TILE_THREADS, 0, stream>>>(
             J.A, J.B, J.nA, J.nB, J.nRB, J.nBC, J.gch, clear_p, clear_words, clear_stride, J);
 }
 
@@ -1518,10 +1551,12 @@ void launch_pair(Job &J, const Plan &p, const uint8_t *A, int nA, const uint8_t 
         // (the cleared region is a few MiB at most: its 16-byte word count
         // fits 32 bits)
         const uint32_t words = (uint32_t)C.words;
-        if (cols)
-            launch_fused<true>(J, C.p, words, C.stride, p.units(), stream, e0, e1);
+        if (!cols)
+            launch_fused<false, false>(J, C.p, words, C.stride, p.units(), stream, e0, e1);
+        else if (J.cb32)
+            launch_fused<true, true>(J, C.p, words, C.stride, p.units(), stream, e0, e1);
         else
-            launch_fused<false>(J, C.p, words, C.stride, p.units(), stream, e0, e1);
+            launch_fused<true, false>(J, C.p, words, C.stride, p.units(), stream, e0, e1);
         return;
     }
     uint8_t *q = prep;
@@ -1692,13 +1727,17 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
         prepBlocks = std::max(prepBlocks, prep_blocks(pjobs[k]));
     }
     uint8_t *q = next_region(w);
+    bool narrow = true;                      // 32-bit column bests for every pair of the batch
     for (int k = 0; k < nlive; ++k) {
         const serac_pair pr = pairs[live[k]];
         fill_job(jobs[k], plans[k], desc[pr.a], n[pr.a], pjobs[slot[pr.a]], desc[pr.b], n[pr.b],
                  pjobs[slot[pr.b]], q, rq, out[live[k]].matches, out[live[k]].count);
+        narrow = narrow && jobs[k].cb32;
         q += plans[k].acc;
         rq += plans[k].scratch;
     }
+    for (int k = 0; k < nlive; ++k)          // one sweep kernel: one format for all pairs
+        jobs[k].cb32 = narrow ? 1 : 0;
     for (size_t k = 0; k < zero.size(); ++k)
         zp[k] = zero[k];
     hipError_t e = hipMemcpyAsync(w->aux, host, host_bytes, hipMemcpyHostToDevice, stream);
@@ -1720,12 +1759,15 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
         hipEvent_t e0, e1;
         prof_slot(e0, e1);
         const dim3 grid(nlive * unitsPerJob);
-        if (params->cross_check)
-            hipExtLaunchKernelGGL(serac_tiles_many<true>, grid, dim3(TILE_THREADS), 0, stream,
-                                  e0, e1, 0, djobs, unitsPerJob);
+        if (!params->cross_check)
+            hipExtLaunchKernelGGL(serac_tiles_many<false, false>, grid, dim3(TILE_THREADS), 0,
+                                  stream, e0, e1, 0, djobs, unitsPerJob);
+        else if (narrow)
+            hipExtLaunchKernelGGL(serac_tiles_many<true, true>, grid, dim3(TILE_THREADS), 0,
+                                  stream, e0, e1, 0, djobs, unitsPerJob);
         else
-            hipExtLaunchKernelGGL(serac_tiles_many<false>, grid, dim3(TILE_THREADS), 0, stream,
-                                  e0, e1, 0, djobs, unitsPerJob);
+            hipExtLaunchKernelGGL(serac_tiles_many<true, false>, grid, dim3(TILE_THREADS), 0,
+                                  stream, e0, e1, 0, djobs, unitsPerJob);
         serac_finish_many<<<nlive * gatePerJob, GATE_THREADS, 0, stream>>>(djobs, gatePerJob,
                                                                           G);
     }

@@ -301,6 +301,34 @@ def test_batch_48x8192(serac):
             assert t <= {tuple(x) for x in want.astype(np.int64).tolist()}
 
 
+def test_batch_mixed_sizes(serac):
+    """A batch whose images straddle 8192 rows: pairs whose first image has
+    more than 8192 rows need 64-bit column bests, so the whole batch uses
+    them; every pair against the oracle, cross-check on and off."""
+    rng = np.random.default_rng(91)
+    sizes = (9000, 300, 1200, 8192)
+    imgs_np = [synth.desc(rng, n) for n in sizes]
+    # plant shared rows so that every pair matches some
+    for k in range(1, len(sizes)):
+        imgs_np[k][:40] = imgs_np[0][:40]
+        imgs_np[k][40:60] = imgs_np[0][k * 50:k * 50 + 20]
+    imgs = [dev(x) for x in imgs_np]
+    pairs = [(a, b) for a in range(len(sizes)) for b in range(len(sizes)) if a != b]
+    for cross in (True, False):
+        say(f"[parity] mixed-size batch, cross-check {cross}")
+        res = serac.match_pairs(imgs, pairs, 0.8, math.inf, cross)
+        for k, (a, b) in enumerate(pairs):
+            want = oracle.match_pair(imgs_np[a], imgs_np[b], 0.8, math.inf, cross)
+            assert res[k].cpu().numpy().astype(np.uint32).tobytes() == want.tobytes(), (a, b)
+    # without the large image the batch keeps 32-bit column bests
+    small = [1, 2, 3]
+    pairs2 = [(a, b) for a in small for b in small if a != b]
+    res = serac.match_pairs(imgs, pairs2, 0.8, math.inf, True)
+    for k, (a, b) in enumerate(pairs2):
+        want = oracle.match_pair(imgs_np[a], imgs_np[b], 0.8, math.inf, True)
+        assert res[k].cpu().numpy().astype(np.uint32).tobytes() == want.tobytes(), (a, b)
+
+
 # A single pair is swept straight from the raw descriptors up to 2^27
 # products and through the preparation kernel above; both sides of the
 # switch, with ragged tails.
