@@ -19,6 +19,13 @@ readings are not meaningful (the profiler takes over the dispatch
 timestamps), so there the profiler's own kernel trace is the measurement.
 `cpu_baseline` is the oracle on this host's cores, timed on a bounded
 number of full-pair runs.
+
+`--host-pipeline` measures instead the exhaustive 48-image batch (1128
+pairs of 8192 x 8192) delivered to host memory by serac_match_pairs_host,
+per pair, at several stage sizes: one stage of all pairs is the unpipelined
+order (match everything, then copy), smaller stages overlap the copies and
+the host's unpacking with the matching of later stages.  The device-only
+batch (serac_match_pairs, results left on the device) is timed beside it.
 """
 from __future__ import annotations
 
@@ -88,6 +95,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-every", type=int, default=PROFILE_EVERY, metavar="K",
                     help="attach timing events to one tile-kernel launch in K")
+    ap.add_argument("--host-pipeline", action="store_true",
+                    help="instead of the benchmark, time the exhaustive batch delivered to "
+                         "host memory at several stage sizes (one JSON line)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, copy a MIB-MiB device buffer 10 times "
                          "(a plain copy kernel of known traffic, for scaling the "
@@ -118,6 +128,8 @@ def main() -> int:
     from sift_descriptor_nearest_amd import synth
 
     serac.library()
+    if args.host_pipeline:
+        return host_pipeline(serac, synth, torch, np)
     dev = torch.device("cuda:0")
     p = synth.workload(args.workload)
     nA, nB = p.A.shape[0], p.B.shape[0]
@@ -183,6 +195,52 @@ def main() -> int:
     print(json.dumps(line), flush=True)
     if "identical_to_oracle" in line and not line["identical_to_oracle"]:
         return 1
+    return 0
+
+
+def host_pipeline(serac, synth, torch, np, reps: int = 5) -> int:
+    """Stage-level time per pair of the exhaustive batch, to host memory."""
+    bt = synth.exhaustive_48x8192()
+    imgs = [torch.from_numpy(x).to("cuda:0") for x in bt.images]
+    pairs = bt.pairs.tolist()
+    prm = bt.params()
+    P = len(pairs)
+
+    def timed(fn):
+        fn()                                   # warm-up (allocations, pinned memory)
+        torch.cuda.synchronize()
+        best = math.inf
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            best = min(best, time.perf_counter() - t0)
+        return best * 1e3 / P
+
+    dev_ms = timed(lambda: serac.match_pairs(imgs, pairs, **prm))
+    stages = {}
+    ref = None
+    for per in (P, 256, 64, 16):
+        stages[per] = timed(lambda: serac.match_pairs_host(imgs, pairs, pairs_per_stage=per, **prm))
+        got = serac.match_pairs_host(imgs, pairs, pairs_per_stage=per, **prm)
+        if ref is None:
+            ref = got
+        elif any(a.tobytes() != b.tobytes() for a, b in zip(ref, got)):
+            print("stage sizes disagree", file=sys.stderr)
+            return 1
+    best = min(stages, key=stages.get)
+    line = {
+        "metric": "ms/pair to host memory, exhaustive 48 x 8192 (1128 pairs)",
+        "value": round(stages[best], 5), "unit": "ms/pair", "higher_is_better": False,
+        "n_gpus": 1, "reps": reps, "timing": "best of reps, wall clock, whole call",
+        "data": "synthetic",
+        "config": {"workload": bt.name, "pairs": P, "pairs_per_stage": best},
+        "stages_ms_per_pair": {str(k): round(v, 5) for k, v in stages.items()},
+        "unpipelined_ms_per_pair": round(stages[P], 5),
+        "device_only_ms_per_pair": round(dev_ms, 5),
+        "matches": int(sum(len(x) for x in ref)),
+    }
+    print(json.dumps(line), flush=True)
     return 0
 
 

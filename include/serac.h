@@ -136,6 +136,35 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n,
                       const serac_matches *out_matches);
 
 /*
+ * Match many pairs and deliver every match list to host memory, the way an
+ * exhaustive matching stage consumes them (README "GPU kernel time": at stage level
+ * much of the wall clock is host-side work around the kernels).  The pairs
+ * run in stages of pairs_per_stage (0: 64) through serac_match_pairs on
+ * params->stream; while the device matches stage s, stage s-1's lists are
+ * copied to pinned host memory on a copy stream of the library's and the
+ * host copies stage s-2's lists out to the caller's arrays.
+ *   desc, n, num_images, pairs, num_pairs, params: as serac_match_pairs.
+ *   host_matches host array [num_pairs] of host pointers; host_matches[p]
+ *                receives pair p's matches, ascending a, and must hold
+ *                n[pairs[p].a] entries (it may be NULL when that is 0).
+ *   host_counts  host int32 [num_pairs]: each pair's count, or -1 where its
+ *                device-side ordering hand-off failed (see serac_matches;
+ *                that pair's list is then not written).
+ * Synchronous: returns once every list is in host memory; the results are
+ * identical to serac_match_pairs'.  Device memory for two stages' results
+ * (at capacity) comes from the stream-ordered pool on params->stream;
+ * pinned host memory for two stages is kept per device between calls.
+ * Calls for one device are serialized by the library.
+ * Errors: those of serac_match_pairs, plus SERAC_ERR_INVALID_ARG for
+ * pairs_per_stage < 0 or missing host arrays.
+ */
+int serac_match_pairs_host(const uint8_t *const *desc, const int32_t *n,
+                           int32_t num_images, const serac_pair *pairs,
+                           int32_t num_pairs, const serac_params *params,
+                           int32_t pairs_per_stage, serac_match *const *host_matches,
+                           int32_t *host_counts);
+
+/*
  * The reductions behind the match list, exported for inspection:
  *   row_top2 device int32 [nA][3] = (best, idx, second) per row of A
  *   col_best device int32 [nB][2] = (best, idx) per row of B

@@ -11,7 +11,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["match_pair", "match_pair_into", "match_pairs", "top2",
+__all__ = ["match_pair", "match_pair_into", "match_pairs", "match_pairs_host", "top2",
            "profile_start", "profile_stop", "SeracError", "library", "LIB_PATH"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,12 +67,17 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
                                     ctypes.POINTER(serac_pair), i32,
                                     ctypes.POINTER(serac_params),
                                     ctypes.POINTER(serac_matches)]
+    L.serac_match_pairs_host.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(i32), i32,
+                                         ctypes.POINTER(serac_pair), i32,
+                                         ctypes.POINTER(serac_params), i32,
+                                         ctypes.POINTER(vp), ctypes.POINTER(i32)]
     L.serac_top2_pair.argtypes = [vp, i32, vp, i32, vp, vp, vp]
     L.serac_profile_start.argtypes = [i32, i32]
     L.serac_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
     L.serac_status_string.argtypes = [ctypes.c_int]
     L.serac_status_string.restype = ctypes.c_char_p
-    for f in (L.serac_match_pair, L.serac_match_pairs, L.serac_top2_pair,
+    for f in (L.serac_match_pair, L.serac_match_pairs, L.serac_match_pairs_host,
+              L.serac_top2_pair,
               L.serac_profile_start, L.serac_profile_stop):
         f.restype = ctypes.c_int
     _lib = L
@@ -180,6 +185,47 @@ def match_pairs(images, pairs, max_ratio=0.8, max_distance=math.inf,
     sizes[0::2] = cnt
     sizes[1::2] = caps - cnt
     return list(torch.split(out, sizes.tolist())[0::2])
+
+
+def match_pairs_host(images, pairs, max_ratio=0.8, max_distance=math.inf,
+                     cross_check=True, pairs_per_stage=0):
+    """Match many pairs and return the match lists in host memory.
+
+    Same inputs and results as match_pairs, but the lists arrive as numpy
+    uint32 [count, 2] arrays: the library overlaps copying finished stages
+    to the host with matching the next ones (serac_match_pairs_host).
+    Returns when every list is on the host.
+    """
+    import numpy as np
+    for k, x in enumerate(images):
+        _check_desc(x, f"images[{k}]")
+    pr = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    P = pr.shape[0]
+    if P == 0:
+        return []
+    if pr.min() < 0 or pr.max() >= len(images):
+        raise SeracError(SERAC_ERR_INVALID_ARG, "serac_match_pairs_host")
+    nimg = np.array([x.shape[0] for x in images], dtype=np.int64)
+    caps = nimg[pr[:, 0]]
+    offs = np.zeros(P + 1, dtype=np.int64)
+    np.cumsum(caps, out=offs[1:])
+    host = np.empty((max(int(offs[-1]), 1), 2), dtype=np.uint32)
+    counts = np.empty(P, dtype=np.int32)
+    ptrs = (ctypes.c_void_p * len(images))(*[x.data_ptr() for x in images])
+    ns = nimg.astype(np.int32)
+    cp = np.ascontiguousarray(pr.astype(np.int32))          # serac_pair [P]
+    hp = (host.ctypes.data + offs[:-1] * 8).astype(np.uint64)
+    prm = _params(max_ratio, max_distance, cross_check, _stream(images[0].device))
+    rc = library().serac_match_pairs_host(
+        ptrs, ns.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(images),
+        cp.ctypes.data_as(ctypes.POINTER(serac_pair)), P, ctypes.byref(prm),
+        int(pairs_per_stage), hp.ctypes.data_as(ctypes.POINTER(ctypes.c_void_p)),
+        counts.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    if rc != SERAC_OK:
+        raise SeracError(rc, "serac_match_pairs_host")
+    if counts.min() < 0:
+        raise SeracError(SERAC_ERR_HIP, "serac_match_pairs_host: ordered output hand-off failed")
+    return [host[offs[q]:offs[q] + counts[q]] for q in range(P)]
 
 
 def top2(a, b):

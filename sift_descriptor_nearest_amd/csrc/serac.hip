@@ -1116,6 +1116,21 @@ struct Profile {
 std::mutex g_prof_mutex;
 Profile g_prof;
 
+// Per-device state of serac_match_pairs_host, reused across its calls (one
+// call at a time per device: `busy`): a copy stream, two events per half of
+// the double buffer and the pinned host memory the results land in.
+struct HostPipe {
+    std::mutex busy;
+    bool ready = false;
+    hipStream_t copy = nullptr;
+    hipEvent_t done[2] = {nullptr, nullptr};     // a stage's matching has run
+    hipEvent_t copied[2] = {nullptr, nullptr};   // its results are in pinned memory
+    uint8_t *pinned = nullptr;
+    size_t pinned_bytes = 0;
+};
+HostPipe g_pipes[64];
+constexpr int HOST_STAGE_PAIRS = 64;     // pairs per pipeline stage unless the caller says
+
 // Event pair for the next tile launch, or nulls when not armed / full.
 void prof_slot(hipEvent_t &start, hipEvent_t &stop)
 {
@@ -1778,6 +1793,152 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
         return hip_fail();
     }
     return SERAC_OK;
+}
+
+int serac_match_pairs_host(const uint8_t *const *desc, const int32_t *n, int32_t num_images,
+                           const serac_pair *pairs, int32_t num_pairs,
+                           const serac_params *params, int32_t pairs_per_stage,
+                           serac_match *const *host_matches, int32_t *host_counts)
+{
+    if (num_images < 0 || num_pairs < 0 || pairs_per_stage < 0 || bad_params(params))
+        return SERAC_ERR_INVALID_ARG;
+    if (num_pairs == 0)
+        return SERAC_OK;
+    if (!desc || !n || !pairs || !host_matches || !host_counts)
+        return SERAC_ERR_INVALID_ARG;
+    for (int k = 0; k < num_images; ++k)
+        if (bad_set(desc[k], n[k]))
+            return SERAC_ERR_INVALID_ARG;
+    for (int q = 0; q < num_pairs; ++q) {
+        const serac_pair pr = pairs[q];
+        if (pr.a < 0 || pr.a >= num_images || pr.b < 0 || pr.b >= num_images)
+            return SERAC_ERR_INVALID_ARG;
+        if (n[pr.a] > 0 && !host_matches[q])
+            return SERAC_ERR_INVALID_ARG;
+    }
+    Device *d = nullptr;
+    int st = device_setup(&d);
+    if (st != SERAC_OK)
+        return st;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return hip_fail();
+    HostPipe &P = g_pipes[dev];
+    std::lock_guard<std::mutex> lock(P.busy);
+    if (!P.ready) {
+        // default priority, like every stream of the library
+        if (hipStreamCreateWithFlags(&P.copy, hipStreamNonBlocking) != hipSuccess)
+            return hip_fail();
+        for (int b = 0; b < 2; ++b)
+            if (hipEventCreateWithFlags(&P.done[b], hipEventDisableTiming) != hipSuccess ||
+                hipEventCreateWithFlags(&P.copied[b], hipEventDisableTiming) != hipSuccess)
+                return hip_fail();
+        P.ready = true;
+    }
+    hipStream_t stream = static_cast<hipStream_t>(params->stream);
+    const int per = pairs_per_stage ? pairs_per_stage : HOST_STAGE_PAIRS;
+    const int stages = (num_pairs + per - 1) / per;
+
+    // A stage's results in one block: the counts, then each pair's matches
+    // at capacity n[a] (the counts are not known when the copy is enqueued).
+    const size_t counts_bytes = align256((size_t)per * 4);
+    std::vector<size_t> off(num_pairs + 1);     // byte offset of each pair's matches in its stage
+    size_t half = 0;
+    for (int s0 = 0; s0 < num_pairs; s0 += per) {
+        size_t o = counts_bytes;
+        for (int q = s0; q < std::min(num_pairs, s0 + per); ++q) {
+            off[q] = o;
+            o += (size_t)n[pairs[q].a] * sizeof(serac_match);
+        }
+        half = std::max(half, align256(o));
+    }
+    if (P.pinned_bytes < 2 * half) {
+        if (P.pinned)
+            (void)hipHostFree(P.pinned);
+        P.pinned = nullptr;
+        P.pinned_bytes = 0;
+        if (hipHostMalloc(reinterpret_cast<void **>(&P.pinned), 2 * half, hipHostMallocDefault) !=
+            hipSuccess) {
+            (void)hipGetLastError();
+            P.pinned = nullptr;
+            return SERAC_ERR_OUT_OF_MEMORY;
+        }
+        P.pinned_bytes = 2 * half;
+    }
+    uint8_t *dbuf = nullptr;
+    if (hipMallocAsync(reinterpret_cast<void **>(&dbuf), 2 * half, stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return SERAC_ERR_OUT_OF_MEMORY;
+    }
+
+    // Stage s runs in half s % 2 of the device and pinned buffers.  The
+    // host enqueues stage s, then waits for stage s-1's copy and unpacks
+    // it, so the device matches stage s while stage s-1 crosses the bus and
+    // the host copies stage s-2's lists out.
+    auto unpack = [&](int s) {
+        const uint8_t *h = P.pinned + (size_t)(s & 1) * half;
+        const int32_t *cnt = reinterpret_cast<const int32_t *>(h);
+        for (int q = s * per; q < std::min(num_pairs, (s + 1) * per); ++q) {
+            const int32_t c = cnt[q - s * per];
+            host_counts[q] = c;
+            if (c > 0)
+                std::memcpy(host_matches[q], h + off[q], (size_t)c * sizeof(serac_match));
+        }
+    };
+    std::vector<serac_matches> outs(per);
+    int rc = SERAC_OK;
+    for (int s = 0; s < stages && rc == SERAC_OK; ++s) {
+        const int b = s & 1, q0 = s * per, m = std::min(per, num_pairs - q0);
+        uint8_t *dst = dbuf + (size_t)b * half;
+        hipError_t e = hipSuccess;
+        if (s >= 2)   // stage s-2's copy out of this half has run
+            e = hipStreamWaitEvent(stream, P.copied[b], 0);
+        for (int k = 0; k < m; ++k) {
+            outs[k].matches = reinterpret_cast<serac_match *>(dst + off[q0 + k]);
+            outs[k].capacity = n[pairs[q0 + k].a];
+            outs[k].count = reinterpret_cast<int32_t *>(dst) + k;
+        }
+        if (e == hipSuccess)
+            rc = serac_match_pairs(desc, n, num_images, pairs + q0, m, params, outs.data());
+        else
+            rc = hip_fail();
+        if (rc != SERAC_OK)
+            break;
+        const size_t used = off[q0 + m - 1] + (size_t)n[pairs[q0 + m - 1].a] * sizeof(serac_match);
+        e = hipEventRecord(P.done[b], stream);
+        if (e == hipSuccess)
+            e = hipStreamWaitEvent(P.copy, P.done[b], 0);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(P.pinned + (size_t)b * half, dst, used, hipMemcpyDeviceToHost,
+                               P.copy);
+        if (e == hipSuccess)
+            e = hipEventRecord(P.copied[b], P.copy);
+        if (e == hipSuccess && s >= 1)
+            e = hipEventSynchronize(P.copied[1 - b]);
+        if (e != hipSuccess) {
+            rc = hip_fail();
+            break;
+        }
+        if (s >= 1)
+            unpack(s - 1);
+    }
+    if (rc == SERAC_OK) {
+        if (hipEventSynchronize(P.copied[(stages - 1) & 1]) == hipSuccess)
+            unpack(stages - 1);
+        else
+            rc = hip_fail();
+    }
+    // the device buffer is freed behind every copy out of it
+    if (rc != SERAC_OK)
+        (void)hipStreamSynchronize(P.copy);
+    if (hipEventRecord(P.done[0], P.copy) != hipSuccess ||
+        hipStreamWaitEvent(stream, P.done[0], 0) != hipSuccess ||
+        hipFreeAsync(dbuf, stream) != hipSuccess) {
+        (void)hipGetLastError();
+        if (rc == SERAC_OK)
+            rc = SERAC_ERR_HIP;
+    }
+    return rc;
 }
 
 int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int32_t nB,

@@ -109,6 +109,31 @@ def test_match_pairs_validation():
     assert L.serac_match_pairs(None, None, 0, None, 0, ok, None) == serac.SERAC_OK
 
 
+def test_match_pairs_host_validation():
+    L = serac.library()
+    ptrs = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    ns = (ctypes.c_int32 * 2)(10, 0)
+    ok = ctypes.byref(_p())
+    counts = (ctypes.c_int32 * 4)()
+
+    def run(pairs, hosts, ns=ns, num_images=2, params=ok, per=0, counts=counts):
+        cp = (serac_pair * len(pairs))(*[serac_pair(*p) for p in pairs])
+        hp = (ctypes.c_void_p * len(hosts))(*hosts)
+        return L.serac_match_pairs_host(ptrs, ns, num_images, cp, len(pairs), params, per, hp,
+                                        counts)
+
+    E = serac.SERAC_ERR_INVALID_ARG
+    assert run([(0, 2)], [FAKE]) == E                     # image index out of range
+    assert run([(0, 1)], [FAKE], per=-1) == E             # stage size
+    assert run([(0, 1)], [None]) == E                     # no host array for 10 matches
+    assert run([(0, 1)], [FAKE], counts=None) == E
+    assert run([(0, 1)], [FAKE], params=ctypes.byref(_p(max_ratio=0.0))) == E
+    assert run([(0, 1)], [FAKE], ns=(ctypes.c_int32 * 2)(-1, 3)) == E
+    assert L.serac_match_pairs_host(ptrs, ns, 2, None, 1, ok, 0, None, counts) == E
+    # no pairs: nothing to do, nothing touched
+    assert L.serac_match_pairs_host(None, None, 0, None, 0, ok, 0, None, None) == serac.SERAC_OK
+
+
 def test_top2_validation():
     L = serac.library()
     E = serac.SERAC_ERR_INVALID_ARG

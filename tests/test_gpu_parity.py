@@ -286,6 +286,10 @@ def test_batch_48x8192(serac):
     say(f"[parity] batch {len(bt.pairs)} pairs")
     res = serac.match_pairs(imgs, bt.pairs.tolist(), **bt.params())
     assert len(res) == len(bt.pairs)
+    # the same lists delivered to host memory by the host pipeline
+    host = serac.match_pairs_host(imgs, bt.pairs.tolist(), **bt.params())
+    for k in range(len(bt.pairs)):
+        assert host[k].tobytes() == res[k].cpu().numpy().astype(np.uint32).tobytes(), k
     # every pair equals the single-pair call on it
     for k, (ia, ib) in enumerate(bt.pairs.tolist()):
         one = serac.match_pair(imgs[ia], imgs[ib], **bt.params())
@@ -299,6 +303,33 @@ def test_batch_48x8192(serac):
         if (ia, ib) in bt.truth:
             t = {tuple(x) for x in bt.truth[(ia, ib)].tolist()}
             assert t <= {tuple(x) for x in want.astype(np.int64).tolist()}
+
+
+def test_pairs_host_mixed(serac):
+    """serac_match_pairs_host: stages of 3 pairs (both halves of its double
+    buffer reused several times, the last stage partial), of 64 (one stage)
+    and the default, on images of mixed sizes including an empty one and a
+    one-row one; every list equals match_pairs', a few the oracle's."""
+    rng = np.random.default_rng(17)
+    sizes = (700, 0, 1300, 257, 2048, 1)
+    imgs_np = [synth.desc(rng, n) for n in sizes]
+    for k in (2, 3, 4):
+        imgs_np[k][:30] = synth.noisy(rng, imgs_np[0][30 * k:30 * k + 30], 3)
+    imgs = [dev(x) for x in imgs_np]
+    pairs = [(a, b) for a in range(len(sizes)) for b in range(len(sizes)) if a != b]
+    ref = [x.cpu().numpy().astype(np.uint32) for x in
+           serac.match_pairs(imgs, pairs, 0.8, 0.7, True)]
+    assert sum(len(x) for x in ref) > 0
+    for per in (3, 64, 0):
+        say(f"[parity] host pipeline, {len(pairs)} pairs, stages of {per}")
+        res = serac.match_pairs_host(imgs, pairs, 0.8, 0.7, True, pairs_per_stage=per)
+        assert len(res) == len(pairs)
+        for k in range(len(pairs)):
+            assert res[k].dtype == np.uint32 and res[k].shape[1:] == (2,)
+            assert res[k].tobytes() == ref[k].tobytes(), (per, pairs[k])
+    for a, b in ((0, 2), (2, 0), (3, 4), (0, 1), (5, 0)):
+        want = oracle.match_pair(imgs_np[a], imgs_np[b], 0.8, 0.7, True)
+        assert res[pairs.index((a, b))].tobytes() == want.tobytes(), (a, b)
 
 
 def test_batch_mixed_sizes(serac):
