@@ -488,8 +488,9 @@ def test_threads_one_stream(serac):
 def test_lookback_failure_reported():
     """The finishing kernel's bounded look-back: with the host forcing it to
     give up at once (SERAC_LOOKBACK_SPIN_LIMIT=-1, read at the first call),
-    the count is -1 and the binding raises; every kernel still exits
-    normally.  Its own process, so the setting stays out of the others."""
+    the count is -1 and the binding raises, also through the host pipeline;
+    every kernel still exits normally.  Its own process, so the setting
+    stays out of the others."""
     import os
     import subprocess
     code = (
@@ -508,6 +509,11 @@ def test_lookback_failure_reported():
         "    print('no error', flush=True)\n"
         "except serac.SeracError as e:\n"
         "    print('raised', e, flush=True)\n"
+        "try:\n"
+        "    serac.match_pairs_host([a, b], [(0, 1), (1, 0)], pairs_per_stage=1)\n"
+        "    print('host: no error', flush=True)\n"
+        "except serac.SeracError as e:\n"
+        "    print('host: raised', e, flush=True)\n"
     ) % (str(__import__('pathlib').Path(__file__).resolve().parents[1]),)
     env = dict(os.environ, SERAC_LOOKBACK_SPIN_LIMIT="-1")
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
@@ -515,6 +521,7 @@ def test_lookback_failure_reported():
     say(r.stdout.strip())
     assert r.returncode == 0, r.stderr[-2000:]
     assert "count -1" in r.stdout and "raised" in r.stdout, r.stdout
+    assert "host: raised" in r.stdout, r.stdout
 
 
 def test_profiled_launches_exact(serac):
