@@ -1377,9 +1377,20 @@ struct Plan {
     int units() const { return nRB * Gc; }
 };
 
-// Workgroups of 256 rows by gch chunks of 256 columns; gch (a power of two,
-// at most 64, so a workgroup's columns stay inside one aligned 16384-column
-// window) is the largest that still yields about `target` workgroups.
+// Workgroups of 256 rows by gch chunks of 256 columns; gch is a power of
+// two, at most 64, so a workgroup's columns stay inside one aligned
+// 16384-column window.
+//   - A batch (cus = 0): the largest gch that still yields about `target`
+//     workgroups for the pair (the batch's pairs fill the device together).
+//   - One pair on a device of `cus` compute units (one workgroup each): the
+//     gch with the shortest estimated sweep, the larger on a tie.  A
+//     workgroup of c chunks takes about 1.25 + c chunk times (prologue and
+//     end of the sweep, measured); the full groups run in rounds of `cus`
+//     workgroups, and the workgroups of a ragged last group run in the
+//     last round's idle units if they fit, else after it.  At 10400 x 10400
+//     this takes one round of 8-chunk workgroups instead of two rounds of
+//     4-chunk ones (-8%), at 12000 x 12000 three rounds of 4 chunks instead
+//     of two of 8 plus a ragged round (-8%).
 //
 // Workgroup u sweeps row block u % nRB against column group u / nRB.
 // Consecutive workgroups go to the eight XCDs in turn, so with nRB a
@@ -1387,15 +1398,31 @@ struct Plan {
 // finishing workgroup of that row block (256 rows each).  Every XCD's L2
 // then fetches all of B; a map giving each XCD a 2-D block of the grid cut
 // the fetched bytes by a third but made both kernels slower (measured).
-Plan make_plan(int nA, int nB, long long target)
+Plan make_plan(int nA, int nB, long long target, int cus = 0)
 {
     Plan p;
     p.nRB = (nA + BLOCK_ROWS - 1) / BLOCK_ROWS;
     p.nBC = (nB + CHUNK - 1) / CHUNK;
     p.gch = MAX_GCH;
     auto groups = [&](int g) { return (p.nBC + g - 1) / g; };
-    while (p.gch > 1 && (long long)p.nRB * groups(p.gch) < target)
-        p.gch >>= 1;
+    if (cus > 0) {
+        double best = 0.0;
+        for (int g = MAX_GCH; g >= 1; g >>= 1) {
+            const long long full = (long long)p.nRB * (p.nBC / g);   // workgroups of g chunks
+            const int r = p.nBC % g;                                  // chunks of the ragged group
+            const long long rounds = (full + cus - 1) / cus;
+            double t = (double)rounds * (1.25 + g);
+            if (r > 0 && rounds * cus - full < p.nRB)
+                t += 1.25 + r;
+            if (g == MAX_GCH || t < best) {
+                best = t;
+                p.gch = g;
+            }
+        }
+    } else {
+        while (p.gch > 1 && (long long)p.nRB * groups(p.gch) < target)
+            p.gch >>= 1;
+    }
     p.Gc = groups(p.gch);
     const size_t gates = (size_t)(nA + GATE_THREADS - 1) / GATE_THREADS;
     p.acc = align256((size_t)nB * 8) + align256(gates * 8);
@@ -1629,7 +1656,7 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int
         serac_zero_counts<<<1, 64, 0, stream>>>(nullptr, out->count, 1);
         return hipGetLastError() == hipSuccess ? SERAC_OK : SERAC_ERR_HIP;
     }
-    const Plan p = make_plan(nA, nB, d->cus);
+    const Plan p = make_plan(nA, nB, 0, d->cus);
     Workspace *w = nullptr;
     std::unique_lock<std::mutex> hold;
     st = get_workspace(stream, p.acc, p.scratch + pair_prep_bytes(nA, nB), &w, hold);
@@ -1954,7 +1981,7 @@ int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int3
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     if (nA == 0 && nB == 0)
         return SERAC_OK;
-    const Plan p = make_plan(std::max(nA, 1), std::max(nB, 1), d->cus);
+    const Plan p = make_plan(std::max(nA, 1), std::max(nB, 1), 0, d->cus);
     Workspace *w = nullptr;
     std::unique_lock<std::mutex> hold;
     st = get_workspace(stream, p.acc, p.scratch + pair_prep_bytes(std::max(nA, 1), std::max(nB, 1)),
