@@ -129,6 +129,11 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB,
  * arrays are read before the call returns (they may be released at once);
  * the library copies what the device needs through pinned memory of its
  * own.  Results are valid once the stream has synchronised.
+ * Device scratch grows with the batch: about 16 bytes per column and 12
+ * per row of each pair (about 230 KiB per 8192 x 8192 pair), plus ~132
+ * bytes per descriptor and role (first or second image of a pair) of each
+ * image used.  Very large pair lists are best
+ * split, or given to serac_match_pairs_host, which runs them in stages.
  */
 int serac_match_pairs(const uint8_t *const *desc, const int32_t *n,
                       int32_t num_images, const serac_pair *pairs,
