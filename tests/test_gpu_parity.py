@@ -360,18 +360,18 @@ def test_batch_mixed_sizes(serac):
         assert res[k].cpu().numpy().astype(np.uint32).tobytes() == want.tobytes(), (a, b)
 
 
-# A single pair is swept straight from the raw descriptors up to 2^27
+# A single pair is swept straight from the raw descriptors up to 2^28
 # products and through the preparation kernel above; both sides of the
 # switch, with ragged tails.
-FUSED_LIMIT = 1 << 27
+FUSED_LIMIT = 1 << 28
 
 
-@pytest.mark.parametrize("nA,nB", [(8192, 16384), (8193, 16384), (4096, 32769)],
-                         ids=["8192x16384", "8193x16384", "4096x32769"])
+@pytest.mark.parametrize("nA,nB", [(16384, 16384), (16385, 16384), (8192, 32769)],
+                         ids=["16384x16384", "16385x16384", "8192x32769"])
 def test_fused_switch(serac, nA, nB):
     path = "fused" if nA * nB <= FUSED_LIMIT else "prepared"
     p = synth.pair(nA, nB, 0.2, 4, seed=nA ^ nB)
-    got = check_pair(serac, p.A, p.B, 0.8, 0.7, True, top2=(nA < 8192),
+    got = check_pair(serac, p.A, p.B, 0.8, 0.7, True, top2=(nA <= 8192),
                      label=f"switch {nA}x{nB} ({path})")
     assert len(got) > 0
 
@@ -457,7 +457,7 @@ def test_threads_one_stream(serac):
     fused pair and a larger prepared pair in turn)."""
     import threading
     p1 = synth.pair(1500, 1300, 0.3, 3, seed=41)
-    p2 = synth.pair(2600, 52000, 0.2, 3, seed=42)       # above 2^27 products: prepared
+    p2 = synth.pair(2600, 104000, 0.2, 3, seed=42)      # above 2^28 products: prepared
     want = [oracle.match_pair(p.A, p.B, 0.8, math.inf, True) for p in (p1, p2)]
     dv = [(dev(p.A), dev(p.B)) for p in (p1, p2)]
     stream = torch.cuda.Stream()
