@@ -26,6 +26,11 @@ per pair, at several stage sizes: one stage of all pairs is the unpipelined
 order (match everything, then copy), smaller stages overlap the copies and
 the host's unpacking with the matching of later stages.  The device-only
 batch (serac_match_pairs, results left on the device) is timed beside it.
+
+`--configs` times every named workload (the parity configurations, the
+README survey's image shape 10400 x 10400, and the exhaustive batch), one
+JSON line each, with the match list checked against the oracle (three
+pairs of the batch).
 """
 from __future__ import annotations
 
@@ -98,6 +103,9 @@ def main() -> int:
     ap.add_argument("--host-pipeline", action="store_true",
                     help="instead of the benchmark, time the exhaustive batch delivered to "
                          "host memory at several stage sizes (one JSON line)")
+    ap.add_argument("--configs", action="store_true",
+                    help="instead of the benchmark, time every named workload (one JSON "
+                         "line each)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, copy a MIB-MiB device buffer 10 times "
                          "(a plain copy kernel of known traffic, for scaling the "
@@ -130,6 +138,8 @@ def main() -> int:
     serac.library()
     if args.host_pipeline:
         return host_pipeline(serac, synth, torch, np)
+    if args.configs:
+        return all_configs(serac, synth, torch, np)
     dev = torch.device("cuda:0")
     p = synth.workload(args.workload)
     nA, nB = p.A.shape[0], p.B.shape[0]
@@ -196,6 +206,73 @@ def main() -> int:
     if "identical_to_oracle" in line and not line["identical_to_oracle"]:
         return 1
     return 0
+
+
+def all_configs(serac, synth, torch, np) -> int:
+    """Per-call device time and oracle identity of every named workload."""
+    import oracle
+    pairs = list(synth.WORKLOADS)
+    ok = True
+
+    def emit(name, nA, nB, us, ops, got_ok, matches, **extra):
+        line = {"config": name, "nA": nA, "nB": nB, "us_per_call": round(us, 3),
+                "tops": round(ops / us / 1e6, 2),
+                "pct_of_peak": round(100.0 * ops / us / 1e6 / PEAK_INT8_TOPS, 2),
+                "matches": matches, "identical_to_oracle": got_ok, **extra}
+        print(json.dumps(line), flush=True)
+
+    for name in pairs + ["survey_10400x10400"]:
+        if name == "survey_10400x10400":
+            p = synth.pair(10400, 10400, 0.20, 4, seed=0)
+            prm = dict(max_ratio=0.8, max_distance=0.7, cross_check=True)
+        else:
+            p = synth.workload(name)
+            prm = p.params()
+        nA, nB = p.A.shape[0], p.B.shape[0]
+        a = torch.from_numpy(p.A).to("cuda:0")
+        b = torch.from_numpy(p.B).to("cuda:0")
+        out = torch.empty((nA, 2), dtype=torch.int32, device="cuda:0")
+        cnt = torch.empty(1, dtype=torch.int32, device="cuda:0")
+        ops = 2.0 * 128 * nA * nB
+        reps = int(min(2000, max(20, 2e-1 / max(ops / 1.5e15, 1e-6))))
+        for _ in range(20):
+            serac.match_pair_into(a, b, out, cnt, **prm)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            serac.match_pair_into(a, b, out, cnt, **prm)
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / reps
+        got = out[: int(cnt.item())].cpu().numpy().astype(np.uint32)
+        want = oracle.match_pair(p.A, p.B, **prm)
+        same = bool(got.tobytes() == want.tobytes())
+        ok = ok and same
+        emit(name, nA, nB, us, ops, same, int(len(got)), calls=reps, **prm)
+
+    bt = synth.exhaustive_48x8192()
+    imgs = [torch.from_numpy(x).to("cuda:0") for x in bt.images]
+    bp = bt.pairs.tolist()
+    res = serac.match_pairs(imgs, bp, **bt.params())
+    torch.cuda.synchronize()
+    best = math.inf
+    for _ in range(5):
+        t0 = time.perf_counter()
+        res = serac.match_pairs(imgs, bp, **bt.params())
+        torch.cuda.synchronize()
+        best = min(best, time.perf_counter() - t0)
+    ops = sum(2.0 * 128 * bt.images[x].shape[0] * bt.images[y].shape[0] for x, y in bp)
+    same = True
+    for x, y in ((0, 1), (0, 2), (20, 47)):
+        k = bp.index([x, y])
+        want = oracle.match_pair(bt.images[x], bt.images[y], **bt.params())
+        same = same and res[k].cpu().numpy().astype(np.uint32).tobytes() == want.tobytes()
+    ok = ok and same
+    emit(bt.name, 8192, 8192, best * 1e6 / len(bp), ops / len(bp), bool(same),
+         int(sum(len(r) for r in res)), pairs=len(bp), timing="per pair, best of 5 calls",
+         oracle_pairs_checked=3)
+    return 0 if ok else 1
 
 
 def host_pipeline(serac, synth, torch, np, reps: int = 5) -> int:
