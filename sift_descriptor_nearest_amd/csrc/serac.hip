@@ -1865,7 +1865,7 @@ int serac_match_pairs_host(const uint8_t *const *desc, const int32_t *n, int32_t
         P.ready = true;
     }
     hipStream_t stream = static_cast<hipStream_t>(params->stream);
-    const int per = pairs_per_stage ? pairs_per_stage : HOST_STAGE_PAIRS;
+    const int per = std::min(pairs_per_stage ? pairs_per_stage : HOST_STAGE_PAIRS, num_pairs);
     const int stages = (num_pairs + per - 1) / per;
 
     // A stage's results in one block: the counts, then each pair's matches
