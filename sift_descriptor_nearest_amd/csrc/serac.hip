@@ -51,7 +51,8 @@
 //     gives the column maximum of those rows; the key's low 9 bits are then
 //     replaced by the 16-row slice number (lowest slice wins) and merged with
 //     an LDS atomic max into a ring of eight chunks, which goes out to the
-//     global column bests (64-bit atomic max) during the sweep.  The exact
+//     global column bests (an atomic max, 32-bit up to 8192 rows of A, else
+//     64-bit) during the sweep.  The exact
 //     lowest row inside the winning slice is settled afterwards from the 15
 //     rows that precede it, compared in registers (an exact product only in
 //     the rare case the bounds leave open).
@@ -61,6 +62,11 @@
 //   * The angle gate reads a table of acos(s / 512^2) built on the host with
 //     the C library's acos, so the double-precision decision is the same
 //     one a CPU makes; the ratio test is one IEEE multiply and compare.
+//   * Host side: one workspace per (device, stream), grow-only and
+//     stream-ordered; a batch stages its job tables through pinned memory
+//     behind an event; serac_match_pairs_host runs a batch in stages and
+//     overlaps the copy of each stage's lists to the host with the
+//     matching of the next.
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
