@@ -47,7 +47,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, published
-PROFILE_EVERY = 8            # tile-kernel launches per event-timed one
+# tile-kernel launches per event-timed one: the event handling slows the
+# enqueueing host, and at 1 in 8 it cost ~0.15 us per step (958 against 966
+# TOPS at 1 in 32 or 1 in 128, same box); the kernel time read is the same
+PROFILE_EVERY = 32
 TRAFFIC = os.path.join(ROOT, "profiles", "traffic_tiles_pair_8192x8192.json")
 KERNEL_SRC = os.path.join(ROOT, "sift_descriptor_nearest_amd", "csrc", "serac.hip")
 
