@@ -99,7 +99,14 @@ def _params(max_ratio, max_distance, cross_check, stream):
 
 
 def _stream(device):
+    """The raw hipStream_t of torch's current stream on `device`.  torch's
+    internal accessor returns it directly (~0.2 us); building the public
+    Stream object costs ~2 us per call, a sixth of an 8192 x 8192 call's
+    host time."""
     import torch
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(device.index if device.index is not None else torch.cuda.current_device())
     return torch.cuda.current_stream(device).cuda_stream
 
 

@@ -524,6 +524,18 @@ def test_lookback_failure_reported():
     assert "host: raised" in r.stdout, r.stdout
 
 
+def test_binding_stream_is_torch_current(serac):
+    """The binding's raw stream handle is torch's current stream, on the
+    default stream and inside a side-stream context."""
+    from sift_descriptor_nearest_amd import _stream
+    d = torch.device("cuda:0")
+    assert _stream(d) == torch.cuda.current_stream(d).cuda_stream
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert _stream(d) == s.cuda_stream == torch.cuda.current_stream(d).cuda_stream
+    assert _stream(torch.device("cuda")) == torch.cuda.current_stream().cuda_stream
+
+
 def test_profiled_launches_exact(serac):
     """Tile launches timed with dispatch-attached events give the same
     results, and the timing is returned for each of them."""
