@@ -161,7 +161,10 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n,
  * pinned host memory for two stages is kept per device between calls.
  * Calls for one device are serialized by the library.
  * Errors: those of serac_match_pairs, plus SERAC_ERR_INVALID_ARG for
- * pairs_per_stage < 0 or missing host arrays.
+ * pairs_per_stage < 0 or missing host arrays.  Argument errors are found
+ * before anything is enqueued.  A runtime error in a stage is returned once
+ * the copies already enqueued have finished: the lists and counts of the
+ * stages before it are written, host_counts of the rest is untouched.
  */
 int serac_match_pairs_host(const uint8_t *const *desc, const int32_t *n,
                            int32_t num_images, const serac_pair *pairs,

@@ -1922,6 +1922,7 @@ int serac_match_pairs_host(const uint8_t *const *desc, const int32_t *n, int32_t
     };
     std::vector<serac_matches> outs(per);
     int rc = SERAC_OK;
+    int copied = 0, unpacked = 0;   // stages whose copy is enqueued / whose lists are out
     for (int s = 0; s < stages && rc == SERAC_OK; ++s) {
         const int b = s & 1, q0 = s * per, m = std::min(per, num_pairs - q0);
         uint8_t *dst = dbuf + (size_t)b * half;
@@ -1948,6 +1949,8 @@ int serac_match_pairs_host(const uint8_t *const *desc, const int32_t *n, int32_t
                                P.copy);
         if (e == hipSuccess)
             e = hipEventRecord(P.copied[b], P.copy);
+        if (e == hipSuccess)
+            copied = s + 1;
         if (e == hipSuccess && s >= 1)
             e = hipEventSynchronize(P.copied[1 - b]);
         if (e != hipSuccess) {
@@ -1955,17 +1958,20 @@ int serac_match_pairs_host(const uint8_t *const *desc, const int32_t *n, int32_t
             break;
         }
         if (s >= 1)
-            unpack(s - 1);
+            unpack(unpacked++);
     }
     if (rc == SERAC_OK) {
         if (hipEventSynchronize(P.copied[(stages - 1) & 1]) == hipSuccess)
-            unpack(stages - 1);
+            unpack(unpacked++);
         else
             rc = hip_fail();
+    } else if (hipStreamSynchronize(P.copy) == hipSuccess) {
+        // a later stage failed: the lists of the stages copied before it
+        // are complete
+        while (unpacked < copied)
+            unpack(unpacked++);
     }
     // the device buffer is freed behind every copy out of it
-    if (rc != SERAC_OK)
-        (void)hipStreamSynchronize(P.copy);
     if (hipEventRecord(P.done[0], P.copy) != hipSuccess ||
         hipStreamWaitEvent(stream, P.done[0], 0) != hipSuccess ||
         hipFreeAsync(dbuf, stream) != hipSuccess) {
