@@ -78,6 +78,7 @@
 #include <algorithm>
 #include <deque>
 #include <mutex>
+#include <new>
 #include <type_traits>
 #include <vector>
 
@@ -1623,6 +1624,21 @@ void launch_pair(Job &J, const Plan &p, const uint8_t *A, int nA, const uint8_t 
     launch_tiles(J, p, cols, stream);
 }
 
+// Runs an entry point's body: no C++ exception crosses the C interface (a
+// failed host allocation is reported as out of memory, anything else as a
+// runtime error).
+template <class F>
+int guarded(F &&body) noexcept
+{
+    try {
+        return body();
+    } catch (const std::bad_alloc &) {
+        return SERAC_ERR_OUT_OF_MEMORY;
+    } catch (...) {
+        return SERAC_ERR_HIP;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -1650,184 +1666,188 @@ const char *serac_status_string(int status)
 int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int32_t nB,
                      const serac_params *params, const serac_matches *out)
 {
-    if (bad_set(descA, nA) || bad_set(descB, nB) || bad_params(params) || !out ||
-        !out->count || (nA > 0 && !out->matches))
-        return SERAC_ERR_INVALID_ARG;
-    if (out->capacity < nA)
-        return SERAC_ERR_CAPACITY;
-    Device *d = nullptr;
-    int st = device_setup(&d);
-    if (st != SERAC_OK)
-        return st;
-    hipStream_t stream = static_cast<hipStream_t>(params->stream);
-    if (nA == 0 || nB == 0) {
-        serac_zero_counts<<<1, 64, 0, stream>>>(nullptr, out->count, 1);
-        return hipGetLastError() == hipSuccess ? SERAC_OK : SERAC_ERR_HIP;
-    }
-    const Plan p = make_plan(nA, nB, 0, d->cus);
-    Workspace *w = nullptr;
-    std::unique_lock<std::mutex> hold;
-    st = get_workspace(stream, p.acc, p.scratch + pair_prep_bytes(nA, nB), &w, hold);
-    if (st != SERAC_OK)
-        return st;
-    Job J;
-    const PrepJob none{};
-    fill_job(J, p, descA, nA, none, descB, nB, none, next_region(w), w->aux, out->matches,
-             out->count);
-    launch_pair(J, p, descA, nA, descB, nB, w->aux + p.scratch, take_clear(w, p.acc),
-                params->cross_check != 0, stream);
-    const Gate G = make_gate(d, params);
-    serac_finish_one<<<(nA + GATE_THREADS - 1) / GATE_THREADS, GATE_THREADS, 0, stream>>>(
-        J.rslot, J.nA, J.nB, J.Gc, J.cbest, G.table, G.cross_check, J, G);
-    if (hipGetLastError() != hipSuccess) {
-        mark_dirty(w);
-        return SERAC_ERR_HIP;
-    }
-    return SERAC_OK;
+    return guarded([&]() -> int {
+        if (bad_set(descA, nA) || bad_set(descB, nB) || bad_params(params) || !out ||
+            !out->count || (nA > 0 && !out->matches))
+            return SERAC_ERR_INVALID_ARG;
+        if (out->capacity < nA)
+            return SERAC_ERR_CAPACITY;
+        Device *d = nullptr;
+        int st = device_setup(&d);
+        if (st != SERAC_OK)
+            return st;
+        hipStream_t stream = static_cast<hipStream_t>(params->stream);
+        if (nA == 0 || nB == 0) {
+            serac_zero_counts<<<1, 64, 0, stream>>>(nullptr, out->count, 1);
+            return hipGetLastError() == hipSuccess ? SERAC_OK : SERAC_ERR_HIP;
+        }
+        const Plan p = make_plan(nA, nB, 0, d->cus);
+        Workspace *w = nullptr;
+        std::unique_lock<std::mutex> hold;
+        st = get_workspace(stream, p.acc, p.scratch + pair_prep_bytes(nA, nB), &w, hold);
+        if (st != SERAC_OK)
+            return st;
+        Job J;
+        const PrepJob none{};
+        fill_job(J, p, descA, nA, none, descB, nB, none, next_region(w), w->aux, out->matches,
+                 out->count);
+        launch_pair(J, p, descA, nA, descB, nB, w->aux + p.scratch, take_clear(w, p.acc),
+                    params->cross_check != 0, stream);
+        const Gate G = make_gate(d, params);
+        serac_finish_one<<<(nA + GATE_THREADS - 1) / GATE_THREADS, GATE_THREADS, 0, stream>>>(
+            J.rslot, J.nA, J.nB, J.Gc, J.cbest, G.table, G.cross_check, J, G);
+        if (hipGetLastError() != hipSuccess) {
+            mark_dirty(w);
+            return SERAC_ERR_HIP;
+        }
+        return SERAC_OK;
+    });
 }
 
 int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_images,
                       const serac_pair *pairs, int32_t num_pairs, const serac_params *params,
                       const serac_matches *out)
 {
-    if (num_images < 0 || num_pairs < 0 || bad_params(params))
-        return SERAC_ERR_INVALID_ARG;
-    if (num_pairs == 0)
-        return SERAC_OK;
-    if (!desc || !n || !pairs || !out)
-        return SERAC_ERR_INVALID_ARG;
-    for (int k = 0; k < num_images; ++k)
-        if (bad_set(desc[k], n[k]))
+    return guarded([&]() -> int {
+        if (num_images < 0 || num_pairs < 0 || bad_params(params))
             return SERAC_ERR_INVALID_ARG;
-    for (int q = 0; q < num_pairs; ++q) {
-        const serac_pair pr = pairs[q];
-        if (pr.a < 0 || pr.a >= num_images || pr.b < 0 || pr.b >= num_images)
+        if (num_pairs == 0)
+            return SERAC_OK;
+        if (!desc || !n || !pairs || !out)
             return SERAC_ERR_INVALID_ARG;
-        if (!out[q].count || (n[pr.a] > 0 && !out[q].matches))
-            return SERAC_ERR_INVALID_ARG;
-        if (out[q].capacity < n[pr.a])
-            return SERAC_ERR_CAPACITY;
-    }
-    Device *d = nullptr;
-    int st = device_setup(&d);
-    if (st != SERAC_OK)
-        return st;
-    hipStream_t stream = static_cast<hipStream_t>(params->stream);
+        for (int k = 0; k < num_images; ++k)
+            if (bad_set(desc[k], n[k]))
+                return SERAC_ERR_INVALID_ARG;
+        for (int q = 0; q < num_pairs; ++q) {
+            const serac_pair pr = pairs[q];
+            if (pr.a < 0 || pr.a >= num_images || pr.b < 0 || pr.b >= num_images)
+                return SERAC_ERR_INVALID_ARG;
+            if (!out[q].count || (n[pr.a] > 0 && !out[q].matches))
+                return SERAC_ERR_INVALID_ARG;
+            if (out[q].capacity < n[pr.a])
+                return SERAC_ERR_CAPACITY;
+        }
+        Device *d = nullptr;
+        int st = device_setup(&d);
+        if (st != SERAC_OK)
+            return st;
+        hipStream_t stream = static_cast<hipStream_t>(params->stream);
 
-    // pairs with an empty side only get a zero count
-    std::vector<int32_t *> zero;
-    std::vector<int> live;
-    std::vector<char> asA(num_images, 0), asB(num_images, 0);
-    for (int q = 0; q < num_pairs; ++q) {
-        if (n[pairs[q].a] == 0 || n[pairs[q].b] == 0) {
-            zero.push_back(out[q].count);
-        } else {
-            live.push_back(q);
-            asA[pairs[q].a] = 1;
-            asB[pairs[q].b] = 1;
+        // pairs with an empty side only get a zero count
+        std::vector<int32_t *> zero;
+        std::vector<int> live;
+        std::vector<char> asA(num_images, 0), asB(num_images, 0);
+        for (int q = 0; q < num_pairs; ++q) {
+            if (n[pairs[q].a] == 0 || n[pairs[q].b] == 0) {
+                zero.push_back(out[q].count);
+            } else {
+                live.push_back(q);
+                asA[pairs[q].a] = 1;
+                asB[pairs[q].b] = 1;
+            }
         }
-    }
-    // every image is prepared once, in the roles its pairs use
-    std::vector<int> prepped;
-    size_t prep_total = 0;
-    for (int k = 0; k < num_images; ++k) {
-        if (asA[k] || asB[k]) {
-            prepped.push_back(k);
-            prep_total += prep_bytes(n[k], asA[k], asB[k]);
+        // every image is prepared once, in the roles its pairs use
+        std::vector<int> prepped;
+        size_t prep_total = 0;
+        for (int k = 0; k < num_images; ++k) {
+            if (asA[k] || asB[k]) {
+                prepped.push_back(k);
+                prep_total += prep_bytes(n[k], asA[k], asB[k]);
+            }
         }
-    }
-    // workgroups per pair: enough to fill the device a few times over
-    const int nlive = (int)live.size();
-    const long long target = nlive ? std::max(1LL, (4LL * d->cus + nlive - 1) / nlive) : 1;
-    std::vector<Plan> plans(nlive);
-    size_t acc_bytes = 0, res_bytes = 0;
-    int unitsPerJob = 1, gatePerJob = 1;
-    for (int k = 0; k < nlive; ++k) {
-        const serac_pair pr = pairs[live[k]];
-        plans[k] = make_plan(n[pr.a], n[pr.b], target);
-        acc_bytes += plans[k].acc;
-        res_bytes += plans[k].scratch;
-        unitsPerJob = std::max(unitsPerJob, plans[k].units());
-        gatePerJob = std::max(gatePerJob, (n[pr.a] + GATE_THREADS - 1) / GATE_THREADS);
-    }
-    const size_t jobs_bytes = align256(sizeof(Job) * (size_t)std::max(nlive, 1));
-    const size_t prepjobs_bytes = align256(sizeof(PrepJob) * std::max<size_t>(prepped.size(), 1));
-    const size_t zero_bytes = align256(sizeof(int32_t *) * zero.size() + 8);
-    const size_t host_bytes = jobs_bytes + prepjobs_bytes + zero_bytes;
-    Workspace *w = nullptr;
-    std::unique_lock<std::mutex> hold;
-    st = get_workspace(stream, acc_bytes, host_bytes + res_bytes + prep_total, &w, hold);
-    if (st != SERAC_OK)
-        return st;
-    uint8_t *host = nullptr;
-    st = get_stage(w, host_bytes, &host);
-    if (st != SERAC_OK)
-        return st;
-    Job *jobs = reinterpret_cast<Job *>(host);
-    PrepJob *pjobs = reinterpret_cast<PrepJob *>(host + jobs_bytes);
-    int32_t **zp = reinterpret_cast<int32_t **>(host + jobs_bytes + prepjobs_bytes);
-    uint8_t *rq = w->aux + host_bytes;
-    uint8_t *pq = rq + res_bytes;
-    std::vector<int> slot(num_images, -1);
-    int prepBlocks = 1;
-    for (size_t k = 0; k < prepped.size(); ++k) {
-        const int im = prepped[k];
-        pjobs[k] = make_prep(desc[im], n[im], asA[im], asB[im], pq);
-        slot[im] = (int)k;
-        prepBlocks = std::max(prepBlocks, prep_blocks(pjobs[k]));
-    }
-    uint8_t *q = next_region(w);
-    bool narrow = true;                      // 32-bit column bests for every pair of the batch
-    for (int k = 0; k < nlive; ++k) {
-        const serac_pair pr = pairs[live[k]];
-        fill_job(jobs[k], plans[k], desc[pr.a], n[pr.a], pjobs[slot[pr.a]], desc[pr.b], n[pr.b],
-                 pjobs[slot[pr.b]], q, rq, out[live[k]].matches, out[live[k]].count);
-        narrow = narrow && jobs[k].cb32;
-        q += plans[k].acc;
-        rq += plans[k].scratch;
-    }
-    for (int k = 0; k < nlive; ++k)          // one sweep kernel: one format for all pairs
-        jobs[k].cb32 = narrow ? 1 : 0;
-    for (size_t k = 0; k < zero.size(); ++k)
-        zp[k] = zero[k];
-    hipError_t e = hipMemcpyAsync(w->aux, host, host_bytes, hipMemcpyHostToDevice, stream);
-    if (e == hipSuccess)
-        e = hipEventRecord(w->staged, stream);   // `stage` is reusable once this has run
-    const Job *djobs = reinterpret_cast<const Job *>(w->aux);
-    const PrepJob *dpjobs = reinterpret_cast<const PrepJob *>(w->aux + jobs_bytes);
-    int32_t *const *dzero =
-        reinterpret_cast<int32_t *const *>(w->aux + jobs_bytes + prepjobs_bytes);
-    if (e == hipSuccess && !zero.empty())
-        serac_zero_counts<<<((int)zero.size() + 255) / 256, 256, 0, stream>>>(dzero, nullptr,
-                                                                         (int)zero.size());
-    if (e == hipSuccess && nlive) {
-        Clear C = take_clear(w, acc_bytes);
-        C.stride = (uint32_t)prepBlocks * PREP_THREADS;
-        serac_prep_many<<<dim3(prepBlocks, (unsigned)prepped.size()), PREP_THREADS, 0, stream>>>(
-            dpjobs, C);
-        const Gate G = make_gate(d, params);
-        hipEvent_t e0, e1;
-        prof_slot(e0, e1);
-        const dim3 grid(nlive * unitsPerJob);
-        if (!params->cross_check)
-            hipExtLaunchKernelGGL(serac_tiles_many<false, false>, grid, dim3(TILE_THREADS), 0,
-                                  stream, e0, e1, 0, djobs, unitsPerJob);
-        else if (narrow)
-            hipExtLaunchKernelGGL(serac_tiles_many<true, true>, grid, dim3(TILE_THREADS), 0,
-                                  stream, e0, e1, 0, djobs, unitsPerJob);
-        else
-            hipExtLaunchKernelGGL(serac_tiles_many<true, false>, grid, dim3(TILE_THREADS), 0,
-                                  stream, e0, e1, 0, djobs, unitsPerJob);
-        serac_finish_many<<<nlive * gatePerJob, GATE_THREADS, 0, stream>>>(djobs, gatePerJob,
-                                                                          G);
-    }
-    if (e == hipSuccess)
-        e = hipGetLastError();
-    if (e != hipSuccess) {
-        mark_dirty(w);
-        return hip_fail();
-    }
-    return SERAC_OK;
+        // workgroups per pair: enough to fill the device a few times over
+        const int nlive = (int)live.size();
+        const long long target = nlive ? std::max(1LL, (4LL * d->cus + nlive - 1) / nlive) : 1;
+        std::vector<Plan> plans(nlive);
+        size_t acc_bytes = 0, res_bytes = 0;
+        int unitsPerJob = 1, gatePerJob = 1;
+        for (int k = 0; k < nlive; ++k) {
+            const serac_pair pr = pairs[live[k]];
+            plans[k] = make_plan(n[pr.a], n[pr.b], target);
+            acc_bytes += plans[k].acc;
+            res_bytes += plans[k].scratch;
+            unitsPerJob = std::max(unitsPerJob, plans[k].units());
+            gatePerJob = std::max(gatePerJob, (n[pr.a] + GATE_THREADS - 1) / GATE_THREADS);
+        }
+        const size_t jobs_bytes = align256(sizeof(Job) * (size_t)std::max(nlive, 1));
+        const size_t prepjobs_bytes = align256(sizeof(PrepJob) * std::max<size_t>(prepped.size(), 1));
+        const size_t zero_bytes = align256(sizeof(int32_t *) * zero.size() + 8);
+        const size_t host_bytes = jobs_bytes + prepjobs_bytes + zero_bytes;
+        Workspace *w = nullptr;
+        std::unique_lock<std::mutex> hold;
+        st = get_workspace(stream, acc_bytes, host_bytes + res_bytes + prep_total, &w, hold);
+        if (st != SERAC_OK)
+            return st;
+        uint8_t *host = nullptr;
+        st = get_stage(w, host_bytes, &host);
+        if (st != SERAC_OK)
+            return st;
+        Job *jobs = reinterpret_cast<Job *>(host);
+        PrepJob *pjobs = reinterpret_cast<PrepJob *>(host + jobs_bytes);
+        int32_t **zp = reinterpret_cast<int32_t **>(host + jobs_bytes + prepjobs_bytes);
+        uint8_t *rq = w->aux + host_bytes;
+        uint8_t *pq = rq + res_bytes;
+        std::vector<int> slot(num_images, -1);
+        int prepBlocks = 1;
+        for (size_t k = 0; k < prepped.size(); ++k) {
+            const int im = prepped[k];
+            pjobs[k] = make_prep(desc[im], n[im], asA[im], asB[im], pq);
+            slot[im] = (int)k;
+            prepBlocks = std::max(prepBlocks, prep_blocks(pjobs[k]));
+        }
+        uint8_t *q = next_region(w);
+        bool narrow = true;                      // 32-bit column bests for every pair of the batch
+        for (int k = 0; k < nlive; ++k) {
+            const serac_pair pr = pairs[live[k]];
+            fill_job(jobs[k], plans[k], desc[pr.a], n[pr.a], pjobs[slot[pr.a]], desc[pr.b], n[pr.b],
+                     pjobs[slot[pr.b]], q, rq, out[live[k]].matches, out[live[k]].count);
+            narrow = narrow && jobs[k].cb32;
+            q += plans[k].acc;
+            rq += plans[k].scratch;
+        }
+        for (int k = 0; k < nlive; ++k)          // one sweep kernel: one format for all pairs
+            jobs[k].cb32 = narrow ? 1 : 0;
+        for (size_t k = 0; k < zero.size(); ++k)
+            zp[k] = zero[k];
+        hipError_t e = hipMemcpyAsync(w->aux, host, host_bytes, hipMemcpyHostToDevice, stream);
+        if (e == hipSuccess)
+            e = hipEventRecord(w->staged, stream);   // `stage` is reusable once this has run
+        const Job *djobs = reinterpret_cast<const Job *>(w->aux);
+        const PrepJob *dpjobs = reinterpret_cast<const PrepJob *>(w->aux + jobs_bytes);
+        int32_t *const *dzero =
+            reinterpret_cast<int32_t *const *>(w->aux + jobs_bytes + prepjobs_bytes);
+        if (e == hipSuccess && !zero.empty())
+            serac_zero_counts<<<((int)zero.size() + 255) / 256, 256, 0, stream>>>(dzero, nullptr,
+                                                                             (int)zero.size());
+        if (e == hipSuccess && nlive) {
+            Clear C = take_clear(w, acc_bytes);
+            C.stride = (uint32_t)prepBlocks * PREP_THREADS;
+            serac_prep_many<<<dim3(prepBlocks, (unsigned)prepped.size()), PREP_THREADS, 0, stream>>>(
+                dpjobs, C);
+            const Gate G = make_gate(d, params);
+            hipEvent_t e0, e1;
+            prof_slot(e0, e1);
+            const dim3 grid(nlive * unitsPerJob);
+            if (!params->cross_check)
+                hipExtLaunchKernelGGL(serac_tiles_many<false, false>, grid, dim3(TILE_THREADS), 0,
+                                      stream, e0, e1, 0, djobs, unitsPerJob);
+            else if (narrow)
+                hipExtLaunchKernelGGL(serac_tiles_many<true, true>, grid, dim3(TILE_THREADS), 0,
+                                      stream, e0, e1, 0, djobs, unitsPerJob);
+            else
+                hipExtLaunchKernelGGL(serac_tiles_many<true, false>, grid, dim3(TILE_THREADS), 0,
+                                      stream, e0, e1, 0, djobs, unitsPerJob);
+            serac_finish_many<<<nlive * gatePerJob, GATE_THREADS, 0, stream>>>(djobs, gatePerJob,
+                                                                              G);
+        }
+        if (e == hipSuccess)
+            e = hipGetLastError();
+        if (e != hipSuccess) {
+            mark_dirty(w);
+            return hip_fail();
+        }
+        return SERAC_OK;
+    });
 }
 
 int serac_match_pairs_host(const uint8_t *const *desc, const int32_t *n, int32_t num_images,
@@ -1835,246 +1855,254 @@ int serac_match_pairs_host(const uint8_t *const *desc, const int32_t *n, int32_t
                            const serac_params *params, int32_t pairs_per_stage,
                            serac_match *const *host_matches, int32_t *host_counts)
 {
-    if (num_images < 0 || num_pairs < 0 || pairs_per_stage < 0 || bad_params(params))
-        return SERAC_ERR_INVALID_ARG;
-    if (num_pairs == 0)
-        return SERAC_OK;
-    if (!desc || !n || !pairs || !host_matches || !host_counts)
-        return SERAC_ERR_INVALID_ARG;
-    for (int k = 0; k < num_images; ++k)
-        if (bad_set(desc[k], n[k]))
+    return guarded([&]() -> int {
+        if (num_images < 0 || num_pairs < 0 || pairs_per_stage < 0 || bad_params(params))
             return SERAC_ERR_INVALID_ARG;
-    for (int q = 0; q < num_pairs; ++q) {
-        const serac_pair pr = pairs[q];
-        if (pr.a < 0 || pr.a >= num_images || pr.b < 0 || pr.b >= num_images)
+        if (num_pairs == 0)
+            return SERAC_OK;
+        if (!desc || !n || !pairs || !host_matches || !host_counts)
             return SERAC_ERR_INVALID_ARG;
-        if (n[pr.a] > 0 && !host_matches[q])
-            return SERAC_ERR_INVALID_ARG;
-    }
-    Device *d = nullptr;
-    int st = device_setup(&d);
-    if (st != SERAC_OK)
-        return st;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return hip_fail();
-    HostPipe &P = g_pipes[dev];
-    std::lock_guard<std::mutex> lock(P.busy);
-    if (!P.ready) {
-        // default priority, like every stream of the library
-        if (hipStreamCreateWithFlags(&P.copy, hipStreamNonBlocking) != hipSuccess)
-            return hip_fail();
-        for (int b = 0; b < 2; ++b)
-            if (hipEventCreateWithFlags(&P.done[b], hipEventDisableTiming) != hipSuccess ||
-                hipEventCreateWithFlags(&P.copied[b], hipEventDisableTiming) != hipSuccess)
-                return hip_fail();
-        P.ready = true;
-    }
-    hipStream_t stream = static_cast<hipStream_t>(params->stream);
-    const int per = std::min(pairs_per_stage ? pairs_per_stage : HOST_STAGE_PAIRS, num_pairs);
-    const int stages = (num_pairs + per - 1) / per;
-
-    // A stage's results in one block: the counts, then each pair's matches
-    // at capacity n[a] (the counts are not known when the copy is enqueued).
-    const size_t counts_bytes = align256((size_t)per * 4);
-    std::vector<size_t> off(num_pairs + 1);     // byte offset of each pair's matches in its stage
-    size_t half = 0;
-    for (int s0 = 0; s0 < num_pairs; s0 += per) {
-        size_t o = counts_bytes;
-        for (int q = s0; q < std::min(num_pairs, s0 + per); ++q) {
-            off[q] = o;
-            o += (size_t)n[pairs[q].a] * sizeof(serac_match);
+        for (int k = 0; k < num_images; ++k)
+            if (bad_set(desc[k], n[k]))
+                return SERAC_ERR_INVALID_ARG;
+        for (int q = 0; q < num_pairs; ++q) {
+            const serac_pair pr = pairs[q];
+            if (pr.a < 0 || pr.a >= num_images || pr.b < 0 || pr.b >= num_images)
+                return SERAC_ERR_INVALID_ARG;
+            if (n[pr.a] > 0 && !host_matches[q])
+                return SERAC_ERR_INVALID_ARG;
         }
-        half = std::max(half, align256(o));
-    }
-    if (P.pinned_bytes < 2 * half) {
-        if (P.pinned)
-            (void)hipHostFree(P.pinned);
-        P.pinned = nullptr;
-        P.pinned_bytes = 0;
-        if (hipHostMalloc(reinterpret_cast<void **>(&P.pinned), 2 * half, hipHostMallocDefault) !=
-            hipSuccess) {
-            (void)hipGetLastError();
+        Device *d = nullptr;
+        int st = device_setup(&d);
+        if (st != SERAC_OK)
+            return st;
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess)
+            return hip_fail();
+        HostPipe &P = g_pipes[dev];
+        std::lock_guard<std::mutex> lock(P.busy);
+        if (!P.ready) {
+            // default priority, like every stream of the library
+            if (hipStreamCreateWithFlags(&P.copy, hipStreamNonBlocking) != hipSuccess)
+                return hip_fail();
+            for (int b = 0; b < 2; ++b)
+                if (hipEventCreateWithFlags(&P.done[b], hipEventDisableTiming) != hipSuccess ||
+                    hipEventCreateWithFlags(&P.copied[b], hipEventDisableTiming) != hipSuccess)
+                    return hip_fail();
+            P.ready = true;
+        }
+        hipStream_t stream = static_cast<hipStream_t>(params->stream);
+        const int per = std::min(pairs_per_stage ? pairs_per_stage : HOST_STAGE_PAIRS, num_pairs);
+        const int stages = (num_pairs + per - 1) / per;
+
+        // A stage's results in one block: the counts, then each pair's matches
+        // at capacity n[a] (the counts are not known when the copy is enqueued).
+        const size_t counts_bytes = align256((size_t)per * 4);
+        std::vector<size_t> off(num_pairs + 1);     // byte offset of each pair's matches in its stage
+        size_t half = 0;
+        for (int s0 = 0; s0 < num_pairs; s0 += per) {
+            size_t o = counts_bytes;
+            for (int q = s0; q < std::min(num_pairs, s0 + per); ++q) {
+                off[q] = o;
+                o += (size_t)n[pairs[q].a] * sizeof(serac_match);
+            }
+            half = std::max(half, align256(o));
+        }
+        if (P.pinned_bytes < 2 * half) {
+            if (P.pinned)
+                (void)hipHostFree(P.pinned);
             P.pinned = nullptr;
+            P.pinned_bytes = 0;
+            if (hipHostMalloc(reinterpret_cast<void **>(&P.pinned), 2 * half, hipHostMallocDefault) !=
+                hipSuccess) {
+                (void)hipGetLastError();
+                P.pinned = nullptr;
+                return SERAC_ERR_OUT_OF_MEMORY;
+            }
+            P.pinned_bytes = 2 * half;
+        }
+        uint8_t *dbuf = nullptr;
+        if (hipMallocAsync(reinterpret_cast<void **>(&dbuf), 2 * half, stream) != hipSuccess) {
+            (void)hipGetLastError();
             return SERAC_ERR_OUT_OF_MEMORY;
         }
-        P.pinned_bytes = 2 * half;
-    }
-    uint8_t *dbuf = nullptr;
-    if (hipMallocAsync(reinterpret_cast<void **>(&dbuf), 2 * half, stream) != hipSuccess) {
-        (void)hipGetLastError();
-        return SERAC_ERR_OUT_OF_MEMORY;
-    }
 
-    // Stage s runs in half s % 2 of the device and pinned buffers.  The
-    // host enqueues stage s, then waits for stage s-1's copy and unpacks
-    // it, so the device matches stage s while stage s-1 crosses the bus and
-    // the host copies stage s-2's lists out.
-    auto unpack = [&](int s) {
-        const uint8_t *h = P.pinned + (size_t)(s & 1) * half;
-        const int32_t *cnt = reinterpret_cast<const int32_t *>(h);
-        for (int q = s * per; q < std::min(num_pairs, (s + 1) * per); ++q) {
-            const int32_t c = cnt[q - s * per];
-            host_counts[q] = c;
-            if (c > 0)
-                std::memcpy(host_matches[q], h + off[q], (size_t)c * sizeof(serac_match));
+        // Stage s runs in half s % 2 of the device and pinned buffers.  The
+        // host enqueues stage s, then waits for stage s-1's copy and unpacks
+        // it, so the device matches stage s while stage s-1 crosses the bus and
+        // the host copies stage s-2's lists out.
+        auto unpack = [&](int s) {
+            const uint8_t *h = P.pinned + (size_t)(s & 1) * half;
+            const int32_t *cnt = reinterpret_cast<const int32_t *>(h);
+            for (int q = s * per; q < std::min(num_pairs, (s + 1) * per); ++q) {
+                const int32_t c = cnt[q - s * per];
+                host_counts[q] = c;
+                if (c > 0)
+                    std::memcpy(host_matches[q], h + off[q], (size_t)c * sizeof(serac_match));
+            }
+        };
+        std::vector<serac_matches> outs(per);
+        int rc = SERAC_OK;
+        int copied = 0, unpacked = 0;   // stages whose copy is enqueued / whose lists are out
+        for (int s = 0; s < stages && rc == SERAC_OK; ++s) {
+            const int b = s & 1, q0 = s * per, m = std::min(per, num_pairs - q0);
+            uint8_t *dst = dbuf + (size_t)b * half;
+            hipError_t e = hipSuccess;
+            if (s >= 2)   // stage s-2's copy out of this half has run
+                e = hipStreamWaitEvent(stream, P.copied[b], 0);
+            for (int k = 0; k < m; ++k) {
+                outs[k].matches = reinterpret_cast<serac_match *>(dst + off[q0 + k]);
+                outs[k].capacity = n[pairs[q0 + k].a];
+                outs[k].count = reinterpret_cast<int32_t *>(dst) + k;
+            }
+            if (e == hipSuccess)
+                rc = serac_match_pairs(desc, n, num_images, pairs + q0, m, params, outs.data());
+            else
+                rc = hip_fail();
+            if (rc != SERAC_OK)
+                break;
+            const size_t used = off[q0 + m - 1] + (size_t)n[pairs[q0 + m - 1].a] * sizeof(serac_match);
+            e = hipEventRecord(P.done[b], stream);
+            if (e == hipSuccess)
+                e = hipStreamWaitEvent(P.copy, P.done[b], 0);
+            if (e == hipSuccess)
+                e = hipMemcpyAsync(P.pinned + (size_t)b * half, dst, used, hipMemcpyDeviceToHost,
+                                   P.copy);
+            if (e == hipSuccess)
+                e = hipEventRecord(P.copied[b], P.copy);
+            if (e == hipSuccess)
+                copied = s + 1;
+            if (e == hipSuccess && s >= 1)
+                e = hipEventSynchronize(P.copied[1 - b]);
+            if (e != hipSuccess) {
+                rc = hip_fail();
+                break;
+            }
+            if (s >= 1)
+                unpack(unpacked++);
         }
-    };
-    std::vector<serac_matches> outs(per);
-    int rc = SERAC_OK;
-    int copied = 0, unpacked = 0;   // stages whose copy is enqueued / whose lists are out
-    for (int s = 0; s < stages && rc == SERAC_OK; ++s) {
-        const int b = s & 1, q0 = s * per, m = std::min(per, num_pairs - q0);
-        uint8_t *dst = dbuf + (size_t)b * half;
-        hipError_t e = hipSuccess;
-        if (s >= 2)   // stage s-2's copy out of this half has run
-            e = hipStreamWaitEvent(stream, P.copied[b], 0);
-        for (int k = 0; k < m; ++k) {
-            outs[k].matches = reinterpret_cast<serac_match *>(dst + off[q0 + k]);
-            outs[k].capacity = n[pairs[q0 + k].a];
-            outs[k].count = reinterpret_cast<int32_t *>(dst) + k;
+        if (rc == SERAC_OK) {
+            if (hipEventSynchronize(P.copied[(stages - 1) & 1]) == hipSuccess)
+                unpack(unpacked++);
+            else
+                rc = hip_fail();
+        } else if (hipStreamSynchronize(P.copy) == hipSuccess) {
+            // a later stage failed: the lists of the stages copied before it
+            // are complete
+            while (unpacked < copied)
+                unpack(unpacked++);
         }
-        if (e == hipSuccess)
-            rc = serac_match_pairs(desc, n, num_images, pairs + q0, m, params, outs.data());
-        else
-            rc = hip_fail();
-        if (rc != SERAC_OK)
-            break;
-        const size_t used = off[q0 + m - 1] + (size_t)n[pairs[q0 + m - 1].a] * sizeof(serac_match);
-        e = hipEventRecord(P.done[b], stream);
-        if (e == hipSuccess)
-            e = hipStreamWaitEvent(P.copy, P.done[b], 0);
-        if (e == hipSuccess)
-            e = hipMemcpyAsync(P.pinned + (size_t)b * half, dst, used, hipMemcpyDeviceToHost,
-                               P.copy);
-        if (e == hipSuccess)
-            e = hipEventRecord(P.copied[b], P.copy);
-        if (e == hipSuccess)
-            copied = s + 1;
-        if (e == hipSuccess && s >= 1)
-            e = hipEventSynchronize(P.copied[1 - b]);
-        if (e != hipSuccess) {
-            rc = hip_fail();
-            break;
+        // the device buffer is freed behind every copy out of it
+        if (hipEventRecord(P.done[0], P.copy) != hipSuccess ||
+            hipStreamWaitEvent(stream, P.done[0], 0) != hipSuccess ||
+            hipFreeAsync(dbuf, stream) != hipSuccess) {
+            (void)hipGetLastError();
+            if (rc == SERAC_OK)
+                rc = SERAC_ERR_HIP;
         }
-        if (s >= 1)
-            unpack(unpacked++);
-    }
-    if (rc == SERAC_OK) {
-        if (hipEventSynchronize(P.copied[(stages - 1) & 1]) == hipSuccess)
-            unpack(unpacked++);
-        else
-            rc = hip_fail();
-    } else if (hipStreamSynchronize(P.copy) == hipSuccess) {
-        // a later stage failed: the lists of the stages copied before it
-        // are complete
-        while (unpacked < copied)
-            unpack(unpacked++);
-    }
-    // the device buffer is freed behind every copy out of it
-    if (hipEventRecord(P.done[0], P.copy) != hipSuccess ||
-        hipStreamWaitEvent(stream, P.done[0], 0) != hipSuccess ||
-        hipFreeAsync(dbuf, stream) != hipSuccess) {
-        (void)hipGetLastError();
-        if (rc == SERAC_OK)
-            rc = SERAC_ERR_HIP;
-    }
-    return rc;
+        return rc;
+    });
 }
 
 int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int32_t nB,
                     void *stream_, int32_t *row_top2, int32_t *col_best)
 {
-    if (bad_set(descA, nA) || bad_set(descB, nB) || (nA > 0 && !row_top2) ||
-        (nB > 0 && !col_best))
-        return SERAC_ERR_INVALID_ARG;
-    Device *d = nullptr;
-    int st = device_setup(&d);
-    if (st != SERAC_OK)
-        return st;
-    hipStream_t stream = static_cast<hipStream_t>(stream_);
-    if (nA == 0 && nB == 0)
+    return guarded([&]() -> int {
+        if (bad_set(descA, nA) || bad_set(descB, nB) || (nA > 0 && !row_top2) ||
+            (nB > 0 && !col_best))
+            return SERAC_ERR_INVALID_ARG;
+        Device *d = nullptr;
+        int st = device_setup(&d);
+        if (st != SERAC_OK)
+            return st;
+        hipStream_t stream = static_cast<hipStream_t>(stream_);
+        if (nA == 0 && nB == 0)
+            return SERAC_OK;
+        const Plan p = make_plan(std::max(nA, 1), std::max(nB, 1), 0, d->cus);
+        Workspace *w = nullptr;
+        std::unique_lock<std::mutex> hold;
+        st = get_workspace(stream, p.acc, p.scratch + pair_prep_bytes(std::max(nA, 1), std::max(nB, 1)),
+                           &w, hold);
+        if (st != SERAC_OK)
+            return st;
+        Job J;
+        const PrepJob none{};
+        fill_job(J, p, descA, nA, none, descB, nB, none, next_region(w), w->aux, nullptr, nullptr);
+        // with an empty side nothing is raised: rows report (0, -1, 0) and
+        // columns (0, -1) from the cleared accumulators
+        if (nA > 0 && nB > 0)
+            // the export clears the column accumulators: nothing stays raised
+            launch_pair(J, p, descA, nA, descB, nB, w->aux + p.scratch, take_clear(w, 0), true,
+                        stream);
+        if (nA > 0)
+            serac_export_rows<<<(nA + 255) / 256, 256, 0, stream>>>(J, row_top2);
+        if (nB > 0)
+            serac_export_cols<<<(nB + 255) / 256, 256, 0, stream>>>(J, col_best);
+        if (hipGetLastError() != hipSuccess) {
+            mark_dirty(w);
+            return SERAC_ERR_HIP;
+        }
         return SERAC_OK;
-    const Plan p = make_plan(std::max(nA, 1), std::max(nB, 1), 0, d->cus);
-    Workspace *w = nullptr;
-    std::unique_lock<std::mutex> hold;
-    st = get_workspace(stream, p.acc, p.scratch + pair_prep_bytes(std::max(nA, 1), std::max(nB, 1)),
-                       &w, hold);
-    if (st != SERAC_OK)
-        return st;
-    Job J;
-    const PrepJob none{};
-    fill_job(J, p, descA, nA, none, descB, nB, none, next_region(w), w->aux, nullptr, nullptr);
-    // with an empty side nothing is raised: rows report (0, -1, 0) and
-    // columns (0, -1) from the cleared accumulators
-    if (nA > 0 && nB > 0)
-        // the export clears the column accumulators: nothing stays raised
-        launch_pair(J, p, descA, nA, descB, nB, w->aux + p.scratch, take_clear(w, 0), true,
-                    stream);
-    if (nA > 0)
-        serac_export_rows<<<(nA + 255) / 256, 256, 0, stream>>>(J, row_top2);
-    if (nB > 0)
-        serac_export_cols<<<(nB + 255) / 256, 256, 0, stream>>>(J, col_best);
-    if (hipGetLastError() != hipSuccess) {
-        mark_dirty(w);
-        return SERAC_ERR_HIP;
-    }
-    return SERAC_OK;
+    });
 }
 
 int serac_profile_start(int32_t max_launches, int32_t every)
 {
-    if (max_launches < 1 || max_launches > (1 << 20) || every < 1 || every > (1 << 20))
-        return SERAC_ERR_INVALID_ARG;
-    std::lock_guard<std::mutex> lock(g_prof_mutex);
-    for (hipEvent_t e : g_prof.ev)
-        if (e)
-            (void)hipEventDestroy(e);
-    g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
-    g_prof.used = 0;
-    g_prof.seen = 0;
-    g_prof.every = every;
-    g_prof.armed = false;
-    // Without a system-scope fence: a default event makes its dispatch
-    // write the caches back for the host at the end, which lengthened the
-    // timed launches by ~1.3 us against the untimed ones (profiler trace).
-    for (auto &e : g_prof.ev) {
-        if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
-            e = nullptr;
-            return hip_fail();
+    return guarded([&]() -> int {
+        if (max_launches < 1 || max_launches > (1 << 20) || every < 1 || every > (1 << 20))
+            return SERAC_ERR_INVALID_ARG;
+        std::lock_guard<std::mutex> lock(g_prof_mutex);
+        for (hipEvent_t e : g_prof.ev)
+            if (e)
+                (void)hipEventDestroy(e);
+        g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
+        g_prof.used = 0;
+        g_prof.seen = 0;
+        g_prof.every = every;
+        g_prof.armed = false;
+        // Without a system-scope fence: a default event makes its dispatch
+        // write the caches back for the host at the end, which lengthened the
+        // timed launches by ~1.3 us against the untimed ones (profiler trace).
+        for (auto &e : g_prof.ev) {
+            if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
+                e = nullptr;
+                return hip_fail();
+            }
         }
-    }
-    g_prof.armed = true;
-    return SERAC_OK;
+        g_prof.armed = true;
+        return SERAC_OK;
+    });
 }
 
 int serac_profile_stop(double *tile_kernel_ms, int32_t *launches)
 {
-    if (!tile_kernel_ms || !launches)
-        return SERAC_ERR_INVALID_ARG;
-    std::lock_guard<std::mutex> lock(g_prof_mutex);
-    if (!g_prof.armed)
-        return SERAC_ERR_INVALID_ARG;
-    double total = 0.0;
-    int st = SERAC_OK;
-    for (int k = 0; k < g_prof.used; ++k) {
-        float ms = 0.f;
-        if (hipEventSynchronize(g_prof.ev[2 * k + 1]) != hipSuccess ||
-            hipEventElapsedTime(&ms, g_prof.ev[2 * k], g_prof.ev[2 * k + 1]) != hipSuccess) {
-            st = hip_fail();
-            break;
+    return guarded([&]() -> int {
+        if (!tile_kernel_ms || !launches)
+            return SERAC_ERR_INVALID_ARG;
+        std::lock_guard<std::mutex> lock(g_prof_mutex);
+        if (!g_prof.armed)
+            return SERAC_ERR_INVALID_ARG;
+        double total = 0.0;
+        int st = SERAC_OK;
+        for (int k = 0; k < g_prof.used; ++k) {
+            float ms = 0.f;
+            if (hipEventSynchronize(g_prof.ev[2 * k + 1]) != hipSuccess ||
+                hipEventElapsedTime(&ms, g_prof.ev[2 * k], g_prof.ev[2 * k + 1]) != hipSuccess) {
+                st = hip_fail();
+                break;
+            }
+            total += ms;
         }
-        total += ms;
-    }
-    *tile_kernel_ms = total;
-    *launches = g_prof.used;
-    for (hipEvent_t e : g_prof.ev)
-        if (e)
-            (void)hipEventDestroy(e);
-    g_prof.ev.clear();
-    g_prof.used = 0;
-    g_prof.armed = false;
-    return st;
+        *tile_kernel_ms = total;
+        *launches = g_prof.used;
+        for (hipEvent_t e : g_prof.ev)
+            if (e)
+                (void)hipEventDestroy(e);
+        g_prof.ev.clear();
+        g_prof.used = 0;
+        g_prof.armed = false;
+        return st;
+    });
 }
 
 }  // extern "C"
