@@ -376,6 +376,19 @@ def test_fused_switch(serac, nA, nB):
     assert len(got) > 0
 
 
+@pytest.mark.parametrize("nA,nB", [(10400, 10400), (12000, 12000), (4096, 32769)],
+                         ids=["10400sq", "12000sq", "4096x32769"])
+def test_column_group_plans(serac, nA, nB):
+    """Pairs whose column-group size comes from the sweep-round estimate:
+    10400^2 (fused, 8-chunk groups and a ragged 1-chunk group in one
+    round), 12000^2 (prepared, 4-chunk groups over three rounds and a
+    ragged 3-chunk group), 4096 x 32769 (prepared, 8-chunk groups and a
+    ragged group in a second round)."""
+    p = synth.pair(nA, nB, 0.2, 4, seed=nA + 7 * nB)
+    got = check_pair(serac, p.A, p.B, 0.8, 0.7, True, top2=False, label=f"plan {nA}x{nB}")
+    assert len(got) > 0
+
+
 def test_wide_column_groups(serac):
     """A tall pair gets 64-chunk (16384-column) column groups: column maxima
     leave the 8-chunk LDS ring during the sweep, tile tags use all 9 bits,
