@@ -7,7 +7,9 @@ rad, cross-check on): at this size two kernels, the fused tile kernel
 (gates, cross-check, ordered output).
 Inputs are resident in HBM before the timed region; outputs are
 preallocated, poisoned before the warm-up, and the last step's match list
-is compared byte for byte with the CPU oracle after the timed region.
+is compared byte for byte with the CPU oracle after the timed region.  The
+2000 warm-up steps (~40 ms) bring the device to its steady clock, which
+it reaches only after ~1000 back-to-back steps.
 
 Prints one JSON line.  `value` and `ms_per_step` come from the timed region.
 `roofline` is for the dominant kernel (the fused tile kernel): its average
