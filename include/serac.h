@@ -21,7 +21,10 @@
  *   - Descriptor arrays are device pointers to n rows of exactly 128 bytes,
  *     row-major, 16-byte aligned.  The caller owns them; the library only
  *     reads them.
- *   - Output arrays are device pointers owned by the caller.
+ *   - Output arrays are device pointers owned by the caller: match arrays
+ *     8-byte aligned, int32 arrays and counts 4-byte aligned.  A pointer
+ *     that is NULL where data is needed, or misaligned, is
+ *     SERAC_ERR_INVALID_ARG.
  *   - Work is enqueued on the given HIP stream (NULL = the null stream) and
  *     is asynchronous: results are valid once that stream has synchronised.
  *     Temporary device memory is taken from the device's stream-ordered
@@ -35,6 +38,11 @@
  *     enqueued and no output is written.
  *   - Only gfx950 devices are supported; any other device is refused with
  *     SERAC_ERR_UNSUPPORTED_DEVICE (there is no fallback path).
+ *   - A failed allocation returns SERAC_ERR_OUT_OF_MEMORY; no kernel that
+ *     writes the caller's outputs has been enqueued, and the next call
+ *     tries again.  (For tests, the environment
+ *     variable SERAC_TEST_FAIL_ALLOC, while set, makes every allocation
+ *     the library attempts fail this way.)
  *   - No C++ exception crosses this interface.
  */
 #ifndef SERAC_H
@@ -128,7 +136,9 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB,
  * Asynchronous on params->stream like the other entry points: the host
  * arrays are read before the call returns (they may be released at once);
  * the library copies what the device needs through pinned memory of its
- * own.  Results are valid once the stream has synchronised.
+ * own, a ring of four buffers per stream.  A call blocks only when the
+ * copy made by the batch call four calls earlier on the same stream has
+ * not run yet.  Results are valid once the stream has synchronised.
  * Device scratch grows with the batch: about 16 bytes per column and 12
  * per row of each pair (about 230 KiB per 8192 x 8192 pair), plus ~132
  * bytes per descriptor and role (first or second image of a pair) of each
@@ -182,27 +192,6 @@ int serac_match_pairs_host(const uint8_t *const *desc, const int32_t *n,
 int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB,
                     int32_t nB, void *stream, int32_t *row_top2,
                     int32_t *col_best);
-
-/*
- * Timing of the fused tile kernel (the kernel that does the contraction and
- * the on-the-fly reductions), for benchmarks.  serac_profile_start arms up
- * to max_launches pairs of HIP events; from then on one tile-kernel launch
- * in `every` (the first, then every `every`-th) made by serac_match_pair,
- * serac_match_pairs or serac_top2_pair is dispatched with hipExtLaunchKernel
- * carrying one pair as its start and stop events, recorded by the dispatch
- * itself on the call's stream.  The events carry no system-scope fence, so a
- * timed dispatch ends like an untimed one (a default event would add a cache
- * write-back for the host to it).  The event handling slows the enqueueing
- * host; timing a fraction of the launches keeps the queue as full as
- * without it.  serac_profile_stop waits for the recorded events, returns
- * the summed device time in milliseconds and the number of launches timed,
- * and disarms.  Not thread-safe against concurrent matching calls from
- * other threads.
- * Errors: SERAC_ERR_INVALID_ARG (max_launches or every outside
- * [1, 1048576], NULL outputs, stop without start), SERAC_ERR_HIP.
- */
-int serac_profile_start(int32_t max_launches, int32_t every);
-int serac_profile_stop(double *tile_kernel_ms, int32_t *launches);
 
 /* Human-readable text for a status code (static storage). */
 const char *serac_status_string(int status);

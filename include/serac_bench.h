@@ -1,0 +1,50 @@
+/*
+ * serac_bench.h - benchmark instrumentation exported by libserac.so.
+ *
+ * Not part of the matching interface (serac.h): these calls keep process-wide
+ * state and exist so that a benchmark can time the dominant kernel of the
+ * matcher, the tile sweep that does the int8 contraction and the on-the-fly
+ * reductions, on the stream its launches run on.
+ */
+#ifndef SERAC_BENCH_H
+#define SERAC_BENCH_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * serac_profile_start arms up to max_launches pairs of HIP events; from then
+ * on one tile-kernel launch in `every` (the first, then every `every`-th)
+ * made by serac_match_pair, serac_match_pairs or serac_top2_pair is
+ * dispatched with hipExtLaunchKernel carrying one pair as its start and stop
+ * events, recorded by the dispatch itself on the call's stream.  The events
+ * carry no system-scope fence, so a timed dispatch ends like an untimed one
+ * (a default event adds a cache write-back for the host to its dispatch).
+ * The event handling slows the enqueueing host; timing a fraction of the
+ * launches keeps the queue as full as without it.
+ *
+ * serac_profile_stop waits for the recorded events and returns:
+ *   tile_kernel_ms  the summed device time of the timed launches (ms)
+ *   launches        how many launches were timed
+ *   per_launch_ms   (may be NULL when capacity is 0) the first `capacity`
+ *                   launches' device times, in launch order
+ *   kernel          (may be NULL) static text naming the tile kernel timed,
+ *                   e.g. "serac_tiles_fused<true, true>"; "mixed" if
+ *                   launches of several kernels were timed, "none" if none
+ * and disarms.  Not thread-safe against concurrent matching calls from other
+ * threads.
+ * Errors: SERAC_ERR_INVALID_ARG (max_launches or every outside [1, 1048576],
+ * NULL outputs, capacity < 0, stop without start), SERAC_ERR_HIP.
+ */
+int serac_profile_start(int32_t max_launches, int32_t every);
+int serac_profile_stop(double *tile_kernel_ms, int32_t *launches, float *per_launch_ms,
+                       int32_t capacity, const char **kernel);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SERAC_BENCH_H */

@@ -73,7 +73,9 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          ctypes.POINTER(vp), ctypes.POINTER(i32)]
     L.serac_top2_pair.argtypes = [vp, i32, vp, i32, vp, vp, vp]
     L.serac_profile_start.argtypes = [i32, i32]
-    L.serac_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
+    L.serac_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32),
+                                     ctypes.POINTER(ctypes.c_float), i32,
+                                     ctypes.POINTER(ctypes.c_char_p)]
     L.serac_status_string.argtypes = [ctypes.c_int]
     L.serac_status_string.restype = ctypes.c_char_p
     for f in (L.serac_match_pair, L.serac_match_pairs, L.serac_match_pairs_host,
@@ -91,6 +93,24 @@ def _check_desc(x, name):
         raise ValueError(f"{name} must be a contiguous torch.uint8 CUDA tensor [n, 128]")
     if x.shape[0] > MAX_DESCRIPTORS:
         raise ValueError(f"{name} has more than {MAX_DESCRIPTORS} descriptors")
+    if x.shape[0] and x.data_ptr() % 16:
+        raise ValueError(f"{name} must start on a 16-byte boundary (the kernels read "
+                         "16-byte words); a view at an odd storage offset does not")
+
+
+def _check_out(out, count, nA, device):
+    """out: int32 [>= nA, 2], count: int32 [>= 1], contiguous, on `device`."""
+    import torch
+    for t, name in ((out, "out"), (count, "count")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or not t.is_cuda \
+                or not t.is_contiguous() or t.device != device:
+            raise ValueError(f"{name} must be a contiguous torch.int32 tensor on {device}")
+    if out.dim() != 2 or out.shape[1] != 2 or out.shape[0] < nA:
+        raise ValueError(f"out must have shape [>= {nA}, 2], got {list(out.shape)}")
+    if count.numel() < 1:
+        raise ValueError("count must hold at least one int32")
+    if (nA and out.data_ptr() % 8) or count.data_ptr() % 4:
+        raise ValueError("out must be 8-byte aligned and count 4-byte aligned")
 
 
 def _params(max_ratio, max_distance, cross_check, stream):
@@ -119,6 +139,9 @@ def match_pair_into(a, b, out, count, max_ratio=0.8, max_distance=math.inf,
     """
     _check_desc(a, "a")
     _check_desc(b, "b")
+    if b.device != a.device:
+        raise ValueError("a and b must be on the same device")
+    _check_out(out, count, a.shape[0], a.device)
     s = _stream(a.device) if stream is None else stream
     p = _params(max_ratio, max_distance, cross_check, s)
     m = serac_matches(out.data_ptr(), out.shape[0], count.data_ptr())
@@ -154,6 +177,8 @@ def match_pairs(images, pairs, max_ratio=0.8, max_distance=math.inf,
     import torch
     for k, x in enumerate(images):
         _check_desc(x, f"images[{k}]")
+        if x.device != images[0].device:
+            raise ValueError("all images must be on one device")
     import numpy as np
     pr = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
     P = pr.shape[0]
@@ -206,6 +231,8 @@ def match_pairs_host(images, pairs, max_ratio=0.8, max_distance=math.inf,
     import numpy as np
     for k, x in enumerate(images):
         _check_desc(x, f"images[{k}]")
+        if x.device != images[0].device:
+            raise ValueError("all images must be on one device")
     pr = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
     P = pr.shape[0]
     if P == 0:
@@ -240,6 +267,8 @@ def top2(a, b):
     import torch
     _check_desc(a, "a")
     _check_desc(b, "b")
+    if b.device != a.device:
+        raise ValueError("a and b must be on the same device")
     row = torch.empty((a.shape[0], 3), dtype=torch.int32, device=a.device)
     col = torch.empty((b.shape[0], 2), dtype=torch.int32, device=a.device)
     rc = library().serac_top2_pair(a.data_ptr(), a.shape[0], b.data_ptr(), b.shape[0],
@@ -259,11 +288,39 @@ def profile_start(max_launches: int, every: int = 1) -> None:
         raise SeracError(rc, "serac_profile_start")
 
 
-def profile_stop():
-    """(summed tile-kernel device milliseconds, launches timed); disarms."""
+def profile_stop(capacity: int = 1 << 16):
+    """(summed tile-kernel device ms, launches timed, per-launch ms list,
+    name of the tile kernel timed); disarms."""
     ms = ctypes.c_double(0.0)
     n = ctypes.c_int32(0)
-    rc = library().serac_profile_stop(ctypes.byref(ms), ctypes.byref(n))
+    per = (ctypes.c_float * max(capacity, 1))()
+    name = ctypes.c_char_p()
+    rc = library().serac_profile_stop(ctypes.byref(ms), ctypes.byref(n), per, int(capacity),
+                                      ctypes.byref(name))
     if rc != SERAC_OK:
         raise SeracError(rc, "serac_profile_stop")
-    return ms.value, n.value
+    return ms.value, n.value, list(per[:min(n.value, capacity)]), name.value.decode()
+
+
+PROBE_PATH = os.path.join(HERE, "libserac_probe.so")
+_probe = None
+
+
+def probe_mfma(blocks: int, iters: int, nv: int = 0):
+    """Back-to-back int8 MFMA rate with nv vector instructions per MFMA
+    (libserac_probe.so): (device ms, TOPS, shader clock GHz)."""
+    global _probe
+    if _probe is None:
+        if not os.path.exists(PROBE_PATH):
+            raise RuntimeError(f"{PROBE_PATH} is missing: build it with __graft_entry__.build()")
+        P = ctypes.CDLL(PROBE_PATH)
+        d = ctypes.POINTER(ctypes.c_double)
+        P.serac_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, d, d, d]
+        P.serac_probe_mfma.restype = ctypes.c_int
+        _probe = P
+    ms, tops, ghz = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    rc = _probe.serac_probe_mfma(int(blocks), int(iters), int(nv), ctypes.byref(ms),
+                                 ctypes.byref(tops), ctypes.byref(ghz))
+    if rc != 0:
+        raise RuntimeError(f"serac_probe_mfma failed ({rc})")
+    return ms.value, tops.value, ghz.value

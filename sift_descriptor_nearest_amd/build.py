@@ -9,6 +9,8 @@ ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "serac.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libserac.so")
+PROBE_SRC = os.path.join(HERE, "csrc", "probe.hip")
+PROBE_LIB = os.path.join(HERE, "libserac_probe.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -22,18 +24,31 @@ HIPCC_FLAGS = [
     # pass the first 16 dwords of scalar kernel arguments in SGPRs at wave
     # launch (kernels whose first loads depend on them take them first)
     "-mllvm", "-amdgpu-kernarg-preload-count=16",
+    # an inline-assembly statement that clobbers a register the compiler
+    # reserves (M0, EXEC, VCC, ...) is a build error, not a warning
+    "-Werror=inline-asm",
 ]
 
 
-def build(out: str = LIB, extra: tuple = ()) -> str:
-    """Compile the library (always); returns its path."""
+def _hipcc(src: str, out: str, extra: tuple = ()) -> str:
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
     tmp = out + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, *extra, "-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [hipcc, *HIPCC_FLAGS, *extra, "-I", INCLUDE, src, "-o", tmp]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
 
 
+def build(out: str = LIB, extra: tuple = ()) -> str:
+    """Compile the matcher library (always); returns its path."""
+    return _hipcc(SRC, out, extra)
+
+
+def build_probe(out: str = PROBE_LIB) -> str:
+    """Compile the benchmark's measurement kernels (always); returns the path."""
+    return _hipcc(PROBE_SRC, out)
+
+
 if __name__ == "__main__":
     print(build())
+    print(build_probe())

@@ -83,6 +83,7 @@
 #include <vector>
 
 #include "serac.h"
+#include "serac_bench.h"
 
 namespace {
 
@@ -239,14 +240,16 @@ __device__ __forceinline__ uint32_t bytesum16(uint4 v)
     return __builtin_amdgcn_udot4(v.w, 0x01010101u, s, false);
 }
 
-// Wait until at most `n` vector-memory loads of this wave are outstanding
-// (gfx9 s_waitcnt encoding; exp and lgkm counters left alone).  Loads
-// complete in issue order, so this waits for all but the last n issued.
+// Wait until at most `N` vector-memory loads of this wave are outstanding.
+// Loads complete in issue order, so this waits for all but the last N
+// issued.  Written as inline assembly with a memory clobber, so that the
+// compiler moves no memory access across it: it is what orders the LDS
+// reads of a chunk after that chunk's copy into LDS (see load_lds16).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Workgroup barrier that orders LDS traffic only: waits for this wave's LDS
@@ -264,16 +267,18 @@ typedef __attribute__((address_space(3))) void *lds_void_ptr;
 // the same for the whole wave.
 //
 // Issued as inline assembly so that the compiler does not track the LDS
-// write: it cannot tell the two chunk buffers apart and would otherwise
-// wait for the prefetch of the next chunk before every LDS access that
-// follows it.  Callers order the write themselves (wait_vmcnt, barrier);
-// the compiler's own vmcnt waits stay safe, as extra loads in flight only
-// make them wait longer.
+// write: its tracking of such copies does not survive the branches of the
+// chunk loop, and it would then wait for the prefetch of the next chunk
+// before LDS reads of the other buffer.  The LDS base goes in through an
+// input operand bound to M0, so the compiler itself loads M0 and knows
+// what it holds (nothing is clobbered behind its back).  Callers order the
+// write themselves: wait_vmcnt (a compiler barrier as well) before the
+// reads, and a barrier where other waves read it; the compiler's own vmcnt
+// waits stay safe, as extra loads in flight only make them wait longer.
 __device__ __forceinline__ void load_lds16(const void *src, void *lds_wave_base)
 {
     const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void_ptr)lds_wave_base;
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(src), "s"(m0) : "memory", "m0");
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
 }
 
 // ------------------------------------------------------------ preparation
@@ -1119,6 +1124,7 @@ struct Profile {
     int every = 1;                // time one launch in `every`
     long long seen = 0;           // tile launches since arming
     std::vector<hipEvent_t> ev;   // [2 * max]: start, stop
+    const char *kernel = nullptr; // the kernel timed ("mixed" if several)
 };
 std::mutex g_prof_mutex;
 Profile g_prof;
@@ -1138,8 +1144,9 @@ struct HostPipe {
 HostPipe g_pipes[64];
 constexpr int HOST_STAGE_PAIRS = 64;     // pairs per pipeline stage unless the caller says
 
-// Event pair for the next tile launch, or nulls when not armed / full.
-void prof_slot(hipEvent_t &start, hipEvent_t &stop)
+// Event pair for the next tile launch (a launch of the kernel `kernel`),
+// or nulls when not armed / full.
+void prof_slot(hipEvent_t &start, hipEvent_t &stop, const char *kernel)
 {
     start = stop = nullptr;
     std::lock_guard<std::mutex> lock(g_prof_mutex);
@@ -1150,9 +1157,34 @@ void prof_slot(hipEvent_t &start, hipEvent_t &stop)
     start = g_prof.ev[2 * g_prof.used];
     stop = g_prof.ev[2 * g_prof.used + 1];
     ++g_prof.used;
+    if (!g_prof.kernel)
+        g_prof.kernel = kernel;
+    else if (std::strcmp(g_prof.kernel, kernel) != 0)
+        g_prof.kernel = "mixed";
+}
+
+// Names of the tile kernels as the profiler reports them.
+template <bool COLS, bool NARROW>
+const char *tile_name(bool fused)
+{
+    if (fused)
+        return COLS ? (NARROW ? "serac_tiles_fused<true, true>" : "serac_tiles_fused<true, false>")
+                    : "serac_tiles_fused<false, false>";
+    return COLS ? (NARROW ? "serac_tiles_one<true, true>" : "serac_tiles_one<true, false>")
+                : "serac_tiles_one<false, false>";
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Test hook: while the environment variable SERAC_TEST_FAIL_ALLOC is set,
+// every allocation of device or pinned memory the library would make
+// reports failure instead (SERAC_ERR_OUT_OF_MEMORY), so that tests can
+// check that such a call enqueues nothing and that a later call recovers.
+// Read at each allocation, which only happens when a workspace grows.
+bool fail_alloc()
+{
+    return std::getenv("SERAC_TEST_FAIL_ALLOC") != nullptr;
+}
 
 int hip_fail()
 {
@@ -1170,14 +1202,14 @@ int device_setup(Device **out)
         return SERAC_ERR_UNSUPPORTED_DEVICE;
     std::lock_guard<std::mutex> lock(g_mutex);
     Device &d = g_devices[dev];
+    // Only success and an unsupported device are final; after a transient
+    // failure (a HIP error, the table's allocation) the next call tries again.
     if (!d.init) {
-        d.init = true;
         hipDeviceProp_t prop;
-        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
-            d.status = hip_fail();
-            return d.status;
-        }
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return hip_fail();
         if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+            d.init = true;
             d.status = SERAC_ERR_UNSUPPORTED_DEVICE;
             return d.status;
         }
@@ -1194,16 +1226,14 @@ int device_setup(Device **out)
         std::vector<double> t(NORM2 + 1);
         for (int s = 0; s <= NORM2; ++s)
             t[s] = std::acos(s >= NORM2 ? 1.0 : (double)s / (double)NORM2);
-        if (hipMalloc(&d.table, t.size() * sizeof(double)) != hipSuccess) {
-            d.status = SERAC_ERR_OUT_OF_MEMORY;
+        if (!d.table && (fail_alloc() || hipMalloc(&d.table, t.size() * sizeof(double)) != hipSuccess)) {
             (void)hipGetLastError();
-            return d.status;
+            d.table = nullptr;
+            return SERAC_ERR_OUT_OF_MEMORY;
         }
         if (hipMemcpy(d.table, t.data(), t.size() * sizeof(double), hipMemcpyHostToDevice) !=
-            hipSuccess) {
-            d.status = hip_fail();
-            return d.status;
-        }
+            hipSuccess)
+            return hip_fail();
         hipMemPool_t pool;
         if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
             uint64_t keep = UINT64_MAX;
@@ -1211,6 +1241,7 @@ int device_setup(Device **out)
         }
         (void)hipGetLastError();
         d.status = SERAC_OK;
+        d.init = true;
     }
     *out = &d;
     return d.status;
@@ -1229,9 +1260,13 @@ int device_setup(Device **out)
 //        whole buffer is cleared by a kernel when (re)allocated or after a
 //        failed call;
 //   aux  per-call scratch (the job table of a batch, prepared sets);
-//   stage pinned host memory the job table of a batch is copied from; the
-//        event recorded after that copy tells when it may be rewritten, so
-//        a batch call returns without waiting for its work.
+//   stage a ring of pinned host buffers the job tables of batches are
+//        copied from, each with an event recorded after its copy: a batch
+//        call rewrites the buffer used STAGE_RING calls before, so it waits
+//        only if that call's copy has not run yet (the stream is then at
+//        least STAGE_RING batch calls behind the host).
+constexpr int STAGE_RING = 4;       // pinned staging buffers per workspace
+
 struct Workspace {
     int dev = 0;
     hipStream_t stream = nullptr;
@@ -1242,9 +1277,10 @@ struct Workspace {
     uint8_t *aux = nullptr;
     size_t aux_bytes = 0;
     bool dirty = false;
-    uint8_t *stage = nullptr;
-    size_t stage_bytes = 0;
-    hipEvent_t staged = nullptr;     // recorded after the last copy out of `stage` (or null)
+    uint8_t *stage[STAGE_RING] = {};
+    size_t stage_bytes[STAGE_RING] = {};
+    hipEvent_t staged[STAGE_RING] = {};   // recorded after the copy out of stage[k] (or null)
+    int stage_next = 0;                   // the ring entry the next batch call uses
     std::mutex busy;                 // held by the call enqueueing on this workspace
 };
 std::mutex g_ws_mutex;          // guards the list itself
@@ -1259,7 +1295,7 @@ int grow(uint8_t *&ptr, size_t &have, size_t need, hipStream_t stream, bool clea
     ptr = nullptr;
     have = 0;
     const size_t want = std::max(align256(need), (size_t)1 << 20);
-    if (hipMallocAsync(reinterpret_cast<void **>(&ptr), want, stream) != hipSuccess) {
+    if (fail_alloc() || hipMallocAsync(reinterpret_cast<void **>(&ptr), want, stream) != hipSuccess) {
         (void)hipGetLastError();
         ptr = nullptr;
         return SERAC_ERR_OUT_OF_MEMORY;
@@ -1318,32 +1354,38 @@ int get_workspace(hipStream_t stream, size_t acc_bytes, size_t aux_bytes, Worksp
     return st;
 }
 
-// Pinned staging memory of at least `bytes`, free to be written (the copy
-// out of it that a previous call enqueued has run).
-int get_stage(Workspace *w, size_t bytes, uint8_t **out)
+// The next ring entry of pinned staging memory, at least `bytes`, free to
+// be written: the copy out of it enqueued STAGE_RING batch calls ago has
+// run (waited for here only if it has not).  *ev is to be recorded behind
+// this call's copy out of it.
+int get_stage(Workspace *w, size_t bytes, uint8_t **out, hipEvent_t *ev)
 {
-    if (w->staged && hipEventSynchronize(w->staged) != hipSuccess)
+    const int k = w->stage_next;
+    if (w->staged[k] && hipEventSynchronize(w->staged[k]) != hipSuccess)
         return hip_fail();
-    if (w->stage_bytes < bytes) {
-        if (w->stage)
-            (void)hipHostFree(w->stage);
-        w->stage = nullptr;
-        w->stage_bytes = 0;
-        const size_t want = std::max(align256(bytes), (size_t)1 << 20);
-        if (hipHostMalloc(reinterpret_cast<void **>(&w->stage), want, hipHostMallocDefault) !=
-            hipSuccess) {
+    if (w->stage_bytes[k] < bytes) {
+        if (w->stage[k])
+            (void)hipHostFree(w->stage[k]);
+        w->stage[k] = nullptr;
+        w->stage_bytes[k] = 0;
+        const size_t want = std::max(align256(bytes), (size_t)1 << 16);
+        if (fail_alloc() ||
+            hipHostMalloc(reinterpret_cast<void **>(&w->stage[k]), want, hipHostMallocDefault) !=
+                hipSuccess) {
             (void)hipGetLastError();
-            w->stage = nullptr;
+            w->stage[k] = nullptr;
             return SERAC_ERR_OUT_OF_MEMORY;
         }
-        w->stage_bytes = want;
+        w->stage_bytes[k] = want;
     }
-    if (!w->staged &&
-        hipEventCreateWithFlags(&w->staged, hipEventDisableTiming) != hipSuccess) {
-        w->staged = nullptr;
+    if (!w->staged[k] &&
+        hipEventCreateWithFlags(&w->staged[k], hipEventDisableTiming) != hipSuccess) {
+        w->staged[k] = nullptr;
         return hip_fail();
     }
-    *out = w->stage;
+    w->stage_next = (k + 1) % STAGE_RING;
+    *out = w->stage[k];
+    *ev = w->staged[k];
     return SERAC_OK;
 }
 
@@ -1520,9 +1562,24 @@ bool bad_params(const serac_params *p)
     return p->flags != 0;
 }
 
+bool misaligned(const void *p, uintptr_t align)
+{
+    return ((uintptr_t)p & (align - 1)) != 0;
+}
+
+// A descriptor set: 0 <= n <= the maximum, and for n > 0 a pointer aligned
+// to 16 bytes (the kernels read 16-byte words).
 bool bad_set(const uint8_t *d, int32_t n)
 {
-    return n < 0 || n > SERAC_MAX_DESCRIPTORS || (n > 0 && d == nullptr);
+    return n < 0 || n > SERAC_MAX_DESCRIPTORS || (n > 0 && (d == nullptr || misaligned(d, 16)));
+}
+
+// One pair's output: a count (4-byte aligned) and, when the pair can match,
+// a match array (8-byte aligned: a match is written as one 8-byte word).
+bool bad_out(const serac_matches &o, int32_t nA)
+{
+    return !o.count || misaligned(o.count, 4) ||
+           (nA > 0 && (!o.matches || misaligned(o.matches, 8)));
 }
 
 Gate make_gate(const Device *d, const serac_params *p)
@@ -1537,8 +1594,10 @@ Gate make_gate(const Device *d, const serac_params *p)
 }
 
 template <bool COLS, bool NARROW>
-void launch_one(const Job &J, int units, hipStream_t stream, hipEvent_t e0, hipEvent_t e1)
+void launch_one(const Job &J, int units, hipStream_t stream)
 {
+    hipEvent_t e0, e1;
+    prof_slot(e0, e1, tile_name<COLS, NARROW>(false));
     if (e0)
         hipExtLaunchKernelGGL(serac_tiles_one<COLS, NARROW>, dim3(units), dim3(TILE_THREADS), 0,
                               stream, e0, e1, 0, J);
@@ -1548,14 +1607,12 @@ void launch_one(const Job &J, int units, hipStream_t stream, hipEvent_t e0, hipE
 
 void launch_tiles(const Job &J, const Plan &p, bool cols, hipStream_t stream)
 {
-    hipEvent_t e0, e1;
-    prof_slot(e0, e1);
     if (!cols)
-        launch_one<false, false>(J, p.units(), stream, e0, e1);
+        launch_one<false, false>(J, p.units(), stream);
     else if (J.cb32)
-        launch_one<true, true>(J, p.units(), stream, e0, e1);
+        launch_one<true, true>(J, p.units(), stream);
     else
-        launch_one<true, false>(J, p.units(), stream, e0, e1);
+        launch_one<true, false>(J, p.units(), stream);
 }
 
 // A pair small enough that converting the raw descriptors inside the sweep
@@ -1579,8 +1636,10 @@ size_t pair_prep_bytes(int nA, int nB)
 // The fused sweep, with the timing events e0/e1 attached when not null.
 template <bool COLS, bool NARROW>
 void launch_fused(const Job &J, uint4 *clear_p, uint32_t clear_words, uint32_t clear_stride,
-                  int units, hipStream_t stream, hipEvent_t e0, hipEvent_t e1)
+                  int units, hipStream_t stream)
 {
+    hipEvent_t e0, e1;
+    prof_slot(e0, e1, tile_name<COLS, NARROW>(true));
     if (e0)
         hipExtLaunchKernelGGL(serac_tiles_fused<COLS, NARROW>, dim3(units), dim3(TILE_THREADS), 0,
                               stream, e0, e1, 0, J.A, J.B, J.nA, J.nB, J.nRB, J.nBC, J.gch,
@@ -1597,17 +1656,15 @@ void launch_pair(Job &J, const Plan &p, const uint8_t *A, int nA, const uint8_t 
 {
     if (fused_pair(nA, nB)) {
         C.stride = (uint32_t)p.units() * TILE_THREADS;
-        hipEvent_t e0, e1;
-        prof_slot(e0, e1);
         // (the cleared region is a few MiB at most: its 16-byte word count
         // fits 32 bits)
         const uint32_t words = (uint32_t)C.words;
         if (!cols)
-            launch_fused<false, false>(J, C.p, words, C.stride, p.units(), stream, e0, e1);
+            launch_fused<false, false>(J, C.p, words, C.stride, p.units(), stream);
         else if (J.cb32)
-            launch_fused<true, true>(J, C.p, words, C.stride, p.units(), stream, e0, e1);
+            launch_fused<true, true>(J, C.p, words, C.stride, p.units(), stream);
         else
-            launch_fused<true, false>(J, C.p, words, C.stride, p.units(), stream, e0, e1);
+            launch_fused<true, false>(J, C.p, words, C.stride, p.units(), stream);
         return;
     }
     uint8_t *q = prep;
@@ -1668,7 +1725,7 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int
 {
     return guarded([&]() -> int {
         if (bad_set(descA, nA) || bad_set(descB, nB) || bad_params(params) || !out ||
-            !out->count || (nA > 0 && !out->matches))
+            bad_out(*out, nA))
             return SERAC_ERR_INVALID_ARG;
         if (out->capacity < nA)
             return SERAC_ERR_CAPACITY;
@@ -1722,7 +1779,7 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
             const serac_pair pr = pairs[q];
             if (pr.a < 0 || pr.a >= num_images || pr.b < 0 || pr.b >= num_images)
                 return SERAC_ERR_INVALID_ARG;
-            if (!out[q].count || (n[pr.a] > 0 && !out[q].matches))
+            if (bad_out(out[q], n[pr.a]))
                 return SERAC_ERR_INVALID_ARG;
             if (out[q].capacity < n[pr.a])
                 return SERAC_ERR_CAPACITY;
@@ -1779,7 +1836,8 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
         if (st != SERAC_OK)
             return st;
         uint8_t *host = nullptr;
-        st = get_stage(w, host_bytes, &host);
+        hipEvent_t staged = nullptr;
+        st = get_stage(w, host_bytes, &host, &staged);
         if (st != SERAC_OK)
             return st;
         Job *jobs = reinterpret_cast<Job *>(host);
@@ -1811,7 +1869,7 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
             zp[k] = zero[k];
         hipError_t e = hipMemcpyAsync(w->aux, host, host_bytes, hipMemcpyHostToDevice, stream);
         if (e == hipSuccess)
-            e = hipEventRecord(w->staged, stream);   // `stage` is reusable once this has run
+            e = hipEventRecord(staged, stream);   // the staging buffer is reusable once this has run
         const Job *djobs = reinterpret_cast<const Job *>(w->aux);
         const PrepJob *dpjobs = reinterpret_cast<const PrepJob *>(w->aux + jobs_bytes);
         int32_t *const *dzero =
@@ -1826,7 +1884,10 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
                 dpjobs, C);
             const Gate G = make_gate(d, params);
             hipEvent_t e0, e1;
-            prof_slot(e0, e1);
+            prof_slot(e0, e1,
+                      !params->cross_check ? "serac_tiles_many<false, false>"
+                      : narrow             ? "serac_tiles_many<true, true>"
+                                           : "serac_tiles_many<true, false>");
             const dim3 grid(nlive * unitsPerJob);
             if (!params->cross_check)
                 hipExtLaunchKernelGGL(serac_tiles_many<false, false>, grid, dim3(TILE_THREADS), 0,
@@ -1913,7 +1974,8 @@ int serac_match_pairs_host(const uint8_t *const *desc, const int32_t *n, int32_t
                 (void)hipHostFree(P.pinned);
             P.pinned = nullptr;
             P.pinned_bytes = 0;
-            if (hipHostMalloc(reinterpret_cast<void **>(&P.pinned), 2 * half, hipHostMallocDefault) !=
+            if (fail_alloc() ||
+                hipHostMalloc(reinterpret_cast<void **>(&P.pinned), 2 * half, hipHostMallocDefault) !=
                 hipSuccess) {
                 (void)hipGetLastError();
                 P.pinned = nullptr;
@@ -1922,7 +1984,8 @@ int serac_match_pairs_host(const uint8_t *const *desc, const int32_t *n, int32_t
             P.pinned_bytes = 2 * half;
         }
         uint8_t *dbuf = nullptr;
-        if (hipMallocAsync(reinterpret_cast<void **>(&dbuf), 2 * half, stream) != hipSuccess) {
+        if (fail_alloc() ||
+            hipMallocAsync(reinterpret_cast<void **>(&dbuf), 2 * half, stream) != hipSuccess) {
             (void)hipGetLastError();
             return SERAC_ERR_OUT_OF_MEMORY;
         }
@@ -2008,8 +2071,9 @@ int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int3
                     void *stream_, int32_t *row_top2, int32_t *col_best)
 {
     return guarded([&]() -> int {
-        if (bad_set(descA, nA) || bad_set(descB, nB) || (nA > 0 && !row_top2) ||
-            (nB > 0 && !col_best))
+        if (bad_set(descA, nA) || bad_set(descB, nB) ||
+            (nA > 0 && (!row_top2 || misaligned(row_top2, 4))) ||
+            (nB > 0 && (!col_best || misaligned(col_best, 4))))
             return SERAC_ERR_INVALID_ARG;
         Device *d = nullptr;
         int st = device_setup(&d);
@@ -2060,6 +2124,7 @@ int serac_profile_start(int32_t max_launches, int32_t every)
         g_prof.seen = 0;
         g_prof.every = every;
         g_prof.armed = false;
+        g_prof.kernel = nullptr;
         // Without a system-scope fence: a default event makes its dispatch
         // write the caches back for the host at the end, which lengthened the
         // timed launches by ~1.3 us against the untimed ones (profiler trace).
@@ -2074,10 +2139,11 @@ int serac_profile_start(int32_t max_launches, int32_t every)
     });
 }
 
-int serac_profile_stop(double *tile_kernel_ms, int32_t *launches)
+int serac_profile_stop(double *tile_kernel_ms, int32_t *launches, float *per_launch_ms,
+                       int32_t capacity, const char **kernel)
 {
     return guarded([&]() -> int {
-        if (!tile_kernel_ms || !launches)
+        if (!tile_kernel_ms || !launches || capacity < 0 || (capacity > 0 && !per_launch_ms))
             return SERAC_ERR_INVALID_ARG;
         std::lock_guard<std::mutex> lock(g_prof_mutex);
         if (!g_prof.armed)
@@ -2092,9 +2158,13 @@ int serac_profile_stop(double *tile_kernel_ms, int32_t *launches)
                 break;
             }
             total += ms;
+            if (k < capacity)
+                per_launch_ms[k] = ms;
         }
         *tile_kernel_ms = total;
         *launches = g_prof.used;
+        if (kernel)
+            *kernel = g_prof.kernel ? g_prof.kernel : "none";
         for (hipEvent_t e : g_prof.ev)
             if (e)
                 (void)hipEventDestroy(e);

@@ -211,6 +211,10 @@ WORKLOADS = {
         edge_pair(8192, 96, 48, 5, True, 0), "edge_8192x96_skinny"),
     "edge_8192x96_skinny_no255": lambda: _named(
         edge_pair(8192, 96, 48, 5, False, 0), "edge_8192x96_skinny_no255"),
+    # the feature count per image of the README's 4000x3000 survey
+    # (about 10,400), with the 8192 x 8192 pair's planting and gates
+    "survey_10400x10400": lambda: _named(pair(10400, 10400, 0.20, 4, 0),
+                                         "survey_10400x10400", max_distance=0.7),
 }
 
 

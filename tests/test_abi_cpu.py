@@ -15,19 +15,32 @@ HEADER = os.path.join(ROOT, "include", "serac.h")
 FAKE = 0x10000          # never dereferenced: validation fails first
 
 
-def declared():
-    src = open(HEADER).read()
+def declared(header=HEADER):
+    src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(serac_\w+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_function():
     L = serac.library()
-    names = declared()
+    names = declared() + declared(os.path.join(ROOT, "include", "serac_bench.h"))
     assert {"serac_match_pair", "serac_match_pairs", "serac_top2_pair",
-            "serac_status_string"} <= set(names)
+            "serac_status_string", "serac_profile_start", "serac_profile_stop"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
+
+
+def test_probe_library_exports_its_header():
+    P = ctypes.CDLL(serac.PROBE_PATH)
+    names = declared(os.path.join(ROOT, "include", "serac_probe.h"))
+    assert names == ["serac_probe_mfma"]
+    for name in names:
+        assert hasattr(P, name), name
+
+
+def test_every_header_is_checked():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == \
+        ["serac.h", "serac_bench.h", "serac_probe.h"]
 
 
 def test_status_strings():
@@ -80,6 +93,18 @@ def test_match_pair_rejects_bad_sets():
     assert call_pair(out=ctypes.byref(serac_matches(FAKE, 100, None))) == E
 
 
+def test_match_pair_rejects_misaligned_pointers():
+    """Descriptors must be 16-byte aligned, match arrays 8, counts 4."""
+    E = serac.SERAC_ERR_INVALID_ARG
+    assert call_pair(a=FAKE + 8) == E
+    assert call_pair(b=FAKE + 1) == E
+    assert call_pair(out=ctypes.byref(serac_matches(FAKE + 4, 100, FAKE))) == E
+    assert call_pair(out=ctypes.byref(serac_matches(FAKE, 100, FAKE + 2))) == E
+    L = serac.library()
+    assert L.serac_top2_pair(FAKE, 3, FAKE, 3, None, FAKE + 2, FAKE) == E
+    assert L.serac_top2_pair(FAKE, 3, FAKE, 3, None, FAKE, FAKE + 1) == E
+
+
 def test_match_pair_rejects_small_capacity():
     assert call_pair(nA=101) == serac.SERAC_ERR_CAPACITY
     assert call_pair(nA=10, out=ctypes.byref(_m(9))) == serac.SERAC_ERR_CAPACITY
@@ -102,6 +127,11 @@ def test_match_pairs_validation():
     assert run([(0, 1)], [_m()], params=ctypes.byref(_p(flags=3))) == E
     assert run([(1, 0)], [_m(19)]) == serac.SERAC_ERR_CAPACITY
     assert run([(0, 1)], [serac_matches(FAKE, 100, None)]) == E
+    assert run([(0, 1)], [serac_matches(FAKE + 4, 100, FAKE)]) == E   # misaligned list
+    bad_ptrs = (ctypes.c_void_p * 2)(FAKE, FAKE + 16 + 8)             # misaligned image
+    cp = (serac_pair * 1)(serac_pair(0, 1))
+    ms = (serac_matches * 1)(_m())
+    assert L.serac_match_pairs(bad_ptrs, ns, 2, cp, 1, ok, ms) == E
     bad_n = (ctypes.c_int32 * 2)(10, -1)
     assert run([(0, 1)], [_m()], ns=bad_n) == E
     assert L.serac_match_pairs(ptrs, ns, -1, None, 0, ok, None) == E
@@ -146,3 +176,42 @@ def test_top2_validation():
 def test_binding_rejects_non_tensors():
     with pytest.raises(ValueError):
         serac.match_pair_into(object(), object(), None, None)
+
+
+def test_binding_checks_outputs_and_alignment():
+    """The binding's own checks run before any device work, so they can be
+    exercised with CPU tensors standing in for device ones (is_cuda is
+    patched on the stand-ins)."""
+    import torch
+
+    class Fake(torch.Tensor):
+        @property
+        def is_cuda(self):
+            return True
+
+    def fake(t):
+        return t.as_subclass(Fake)
+
+    a = fake(torch.zeros((4, 128), dtype=torch.uint8))
+    b = fake(torch.zeros((5, 128), dtype=torch.uint8))
+    out = fake(torch.zeros((4, 2), dtype=torch.int32))
+    cnt = fake(torch.zeros(1, dtype=torch.int32))
+    bad = [
+        (fake(torch.zeros((4, 2), dtype=torch.int16)), cnt),      # dtype
+        (fake(torch.zeros(8, dtype=torch.int32)), cnt),           # 1-D
+        (fake(torch.zeros((3, 2), dtype=torch.int32)), cnt),      # too few rows
+        (fake(torch.zeros((4, 4), dtype=torch.int32)[:, :2]), cnt),   # not contiguous
+        (out, fake(torch.zeros(0, dtype=torch.int32))),           # empty count
+        (out, fake(torch.zeros(1, dtype=torch.int64))),           # count dtype
+        (out, torch.zeros(1, dtype=torch.int32)),                 # count not on the device
+    ]
+    for o, c in bad:
+        with pytest.raises(ValueError):
+            serac.match_pair_into(a, b, o, c)
+    # a descriptor view at an odd storage offset is not 16-byte aligned
+    storage = torch.zeros(5 * 128 + 16, dtype=torch.uint8)
+    shift = 8 if storage.data_ptr() % 16 == 0 else 16 - storage.data_ptr() % 16 + 8
+    odd = fake(storage[shift:shift + 4 * 128].view(4, 128))
+    assert odd.data_ptr() % 16 == 8
+    with pytest.raises(ValueError):
+        serac.match_pair_into(odd, b, out, cnt)

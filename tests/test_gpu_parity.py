@@ -555,10 +555,18 @@ def test_profiled_launches_exact(serac):
     p = synth.workload("pair_1000x1200")
     serac.profile_start(8)
     check_pair(serac, p.A, p.B, **p.params(), label="profiled")
-    ms, n = serac.profile_stop()
+    ms, n, per, name = serac.profile_stop()
     assert n == 2 and 0.0 < ms < 1000.0      # one match_pair and one top2 launch
+    assert len(per) == 2 and abs(sum(per) - ms) < 1e-3 * max(ms, 1.0)
+    assert name == "serac_tiles_fused<true, true>"
     serac.profile_start(8, 3)                # every third launch: the 1st and the 4th
     for _ in range(5):
         serac.match_pair(dev(p.A), dev(p.B), **p.params())
-    ms, n = serac.profile_stop()
-    assert n == 2 and 0.0 < ms < 1000.0
+    ms, n, per, name = serac.profile_stop()
+    assert n == 2 and 0.0 < ms < 1000.0 and len(per) == 2
+    # a large pair runs the prepared sweep
+    big = synth.pair(16385, 16384, 0.2, 4, seed=3)
+    serac.profile_start(4)
+    serac.match_pair(dev(big.A), dev(big.B), 0.8, math.inf, False)
+    ms, n, per, name = serac.profile_stop()
+    assert n == 1 and name == "serac_tiles_one<false, false>"
