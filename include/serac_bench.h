@@ -43,6 +43,18 @@ int serac_profile_start(int32_t max_launches, int32_t every);
 int serac_profile_stop(double *tile_kernel_ms, int32_t *launches, float *per_launch_ms,
                        int32_t capacity, const char **kernel);
 
+/*
+ * The current device's angle slack: the finishing kernel of a single pair
+ * takes the ratio and distance gates from the device's double acos where an
+ * interval of this half-width around it settles them, and from the host-built
+ * table (the oracle's libm values) otherwise.  The slack is twice the largest
+ * distance between the two over every attainable score, measured once per
+ * device at set-up, plus 1e-15; +INFINITY (table only) if that check could
+ * not run or while SERAC_TEST_ANGLE_TABLE is set at set-up.
+ * Errors: SERAC_ERR_INVALID_ARG (NULL), those of the device set-up.
+ */
+int serac_angle_slack(double *slack);
+
 #ifdef __cplusplus
 }
 #endif

@@ -76,6 +76,8 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.serac_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32),
                                      ctypes.POINTER(ctypes.c_float), i32,
                                      ctypes.POINTER(ctypes.c_char_p)]
+    L.serac_angle_slack.argtypes = [ctypes.POINTER(ctypes.c_double)]
+    L.serac_angle_slack.restype = ctypes.c_int
     L.serac_status_string.argtypes = [ctypes.c_int]
     L.serac_status_string.restype = ctypes.c_char_p
     for f in (L.serac_match_pair, L.serac_match_pairs, L.serac_match_pairs_host,
@@ -300,6 +302,16 @@ def profile_stop(capacity: int = 1 << 16):
     if rc != SERAC_OK:
         raise SeracError(rc, "serac_profile_stop")
     return ms.value, n.value, list(per[:min(n.value, capacity)]), name.value.decode()
+
+
+def angle_slack() -> float:
+    """Half-width of the interval around the device angle inside which the
+    finishing kernel trusts it (inf: the table decides every gate)."""
+    v = ctypes.c_double(0.0)
+    rc = library().serac_angle_slack(ctypes.byref(v))
+    if rc != SERAC_OK:
+        raise SeracError(rc, "serac_angle_slack")
+    return v.value
 
 
 PROBE_PATH = os.path.join(HERE, "libserac_probe.so")

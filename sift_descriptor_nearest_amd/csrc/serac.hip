@@ -172,9 +172,51 @@ struct Gate {
     const double *table;     // acos(min(s, 512^2) / 512^2), s = 0 .. 512^2
     double max_ratio;
     double max_distance;
+    double slack;            // the device angle is within `slack` of the table (angle_bounds)
     int32_t cross_check;
     int32_t spin_limit;      // look-back polls before giving up (< 0: give up at once)
 };
+
+// Angle of a clamped score computed on the device: the same expression the
+// host table is built from, evaluated with the device's double acos.
+__device__ __forceinline__ double angle_dev(uint32_t s)
+{
+    return acos(s >= (uint32_t)NORM2 ? 1.0 : (double)s / (double)NORM2);
+}
+
+// Deviation of the device angle from the host table over the whole domain
+// (s = 0 .. 512^2): raised into *err as the bits of a non-negative double
+// (which order like the double itself); a NaN counts as infinite.
+__global__ void serac_angle_check(const double *table, unsigned long long *err)
+{
+    const int s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s > NORM2)
+        return;
+    double e = fabs(angle_dev((uint32_t)s) - table[s]);
+    if (!(e == e))
+        e = INFINITY;
+    atomicMax(err, (unsigned long long)__double_as_longlong(e));
+}
+
+// The gates without the table where the device angle settles them: with
+// every device angle within E of the table's, T in [a - slack, a + slack]
+// for slack = 2E + 1e-15 (which also covers the rounding of a +- slack), and
+// the ratio and distance decisions are taken only where the whole interval
+// agrees (max_ratio * x is monotone in x).  1: accept, 0: reject, -1: the
+// table decides.  A NaN angle or slack leaves every comparison false.
+__device__ __forceinline__ int gates_sure(uint32_t S1, uint32_t S2, const Gate &G)
+{
+    const double a1 = angle_dev(S1), a2 = angle_dev(S2);
+    const double lo1 = a1 - G.slack, hi1 = a1 + G.slack;
+    const double lo2 = a2 - G.slack, hi2 = a2 + G.slack;
+    if (lo1 > G.max_distance || lo1 >= G.max_ratio * hi2)
+        return 0;
+    if (hi1 <= G.max_distance && hi1 < G.max_ratio * lo2)
+        return 1;
+    return -1;
+}
+
+
 
 // A row's result over one column group packed into 64 bits, ordered like
 // the key (score first, then lowest column):
@@ -886,6 +928,12 @@ __device__ __forceinline__ void status_store(unsigned long long *p, unsigned lon
 // preparation kernel on this stream clears them before its sweep.  A
 // look-back that does not see its predecessors within the spin limit marks
 // the pair failed: count -1.
+//
+// DEV_ANGLE: the ratio and distance gates are taken from the device's angle
+// where it settles them (gates_sure), computed while the column best of the
+// row's best column is being loaded, so that the table is read only for the
+// rare row the device angle leaves open.
+template <bool DEV_ANGLE, bool NARROW = false>
 __device__ __forceinline__ void finish_body(const Job &J, int wg, int nwg, const Gate &G)
 {
     __shared__ int32_t sWave[GATE_THREADS / 64];
@@ -897,16 +945,40 @@ __device__ __forceinline__ void finish_body(const Job &J, int wg, int nwg, const
     if (i < J.nA)
         row_result(J, i, S1, I1, S2);
     const bool cand = I1 >= 0 && I1 < J.nB;
-    double d1 = 0.0, d2 = 0.0;
     uint32_t C1 = 0u;
     int32_t slice = -1;
-    if (cand) {
-        d1 = G.table[min(S1, (uint32_t)NORM2)];
-        d2 = G.table[min(S2, (uint32_t)NORM2)];
+    bool acc = false;
+    if (DEV_ANGLE) {
+        // the column best is loaded first and decoded last: the device angles
+        // are computed while it is in flight (its width is a template
+        // argument, so the load is issued without a branch)
+        unsigned long long raw = 0ull;
+        if (G.cross_check) {
+            const int j = cand ? I1 : 0;
+            raw = NARROW ? (unsigned long long)reinterpret_cast<const uint32_t *>(J.cbest)[j]
+                         : J.cbest[j];
+        }
+        int sure = gates_sure(S1, S2, G);
+        if (cand && sure < 0) {
+            const double d1 = G.table[min(S1, (uint32_t)NORM2)];
+            const double d2 = G.table[min(S2, (uint32_t)NORM2)];
+            sure = (d1 <= G.max_distance) && (d1 < G.max_ratio * d2);
+        }
+        acc = cand && sure > 0;
+        if (NARROW) {
+            C1 = (uint32_t)raw >> 9;
+            slice = 511 - (int32_t)(raw & 511u);
+        } else {
+            C1 = (uint32_t)(raw >> 32);
+            slice = (int32_t)(0xFFFFFFFFu - (uint32_t)raw);
+        }
+    } else if (cand) {
+        const double d1 = G.table[min(S1, (uint32_t)NORM2)];
+        const double d2 = G.table[min(S2, (uint32_t)NORM2)];
         if (G.cross_check)
             col_best_at(J, I1, C1, slice);
+        acc = (d1 <= G.max_distance) && (d1 < G.max_ratio * d2);
     }
-    bool acc = cand && (d1 <= G.max_distance) && (d1 < G.max_ratio * d2);
     if (G.cross_check) {
         acc = acc && C1 == S1 && slice == i / SLICE;
         // Row i is its column's best only if no lower row of its 16-row
@@ -1011,6 +1083,7 @@ __device__ __forceinline__ void finish_body(const Job &J, int wg, int nwg, const
 
 // The fields read first as leading scalar arguments (preloaded into SGPRs,
 // like the fused sweep's); they override the copies in J and G.
+template <bool NARROW>
 __global__ __launch_bounds__(GATE_THREADS) void serac_finish_one(
     const unsigned long long *rslot, int32_t nA, int32_t nB, int32_t Gc,
     unsigned long long *cbest, const double *table, int32_t cross_check, Job J, Gate G)
@@ -1022,7 +1095,7 @@ __global__ __launch_bounds__(GATE_THREADS) void serac_finish_one(
     J.cbest = cbest;
     G.table = table;
     G.cross_check = cross_check;
-    finish_body(J, blockIdx.x, (J.nA + GATE_THREADS - 1) / GATE_THREADS, G);
+    finish_body<true, NARROW>(J, blockIdx.x, (J.nA + GATE_THREADS - 1) / GATE_THREADS, G);
 }
 
 __global__ __launch_bounds__(GATE_THREADS) void serac_finish_many(const Job *__restrict__ jobs,
@@ -1033,7 +1106,7 @@ __global__ __launch_bounds__(GATE_THREADS) void serac_finish_many(const Job *__r
     const int nwg = (J.nA + GATE_THREADS - 1) / GATE_THREADS;
     if (wg >= nwg)
         return;
-    finish_body(J, wg, nwg, G);
+    finish_body<false>(J, wg, nwg, G);
 }
 
 __global__ void serac_zero_counts(int32_t *const *counts, int32_t *count, int n)
@@ -1109,6 +1182,7 @@ struct Device {
     int status = SERAC_OK;
     int cus = 0;
     double *table = nullptr;
+    double slack = INFINITY;     // device angles are within this of the table (finish_body)
     int spin_limit = FINISH_SPIN_LIMIT;
 };
 
@@ -1192,7 +1266,35 @@ int hip_fail()
     return SERAC_ERR_HIP;
 }
 
-// Per-device set-up: architecture check, acos table, pool threshold.
+// How far the device angle (angle_dev) can be from the host table: the
+// largest deviation over the whole domain, measured once on this device,
+// doubled, plus 1e-15 for the rounding of a +- slack (finish_body).
+// Infinite (every gate decision from the table) if the check cannot run or
+// while the environment variable SERAC_TEST_ANGLE_TABLE is set (a test
+// hook for the table path).
+double angle_slack(const double *table)
+{
+    if (std::getenv("SERAC_TEST_ANGLE_TABLE") || fail_alloc())
+        return INFINITY;
+    unsigned long long *err = nullptr, h = 0;
+    double slack = INFINITY;
+    if (hipMalloc(&err, sizeof(h)) == hipSuccess && hipMemset(err, 0, sizeof(h)) == hipSuccess) {
+        serac_angle_check<<<(NORM2 + 1 + 255) / 256, 256>>>(table, err);
+        if (hipMemcpy(&h, err, sizeof(h), hipMemcpyDeviceToHost) == hipSuccess) {
+            double e;
+            std::memcpy(&e, &h, sizeof(e));
+            if (std::isfinite(e))
+                slack = 2.0 * e + 1e-15;
+        }
+    }
+    if (err)
+        (void)hipFree(err);
+    (void)hipGetLastError();
+    return slack;
+}
+
+// Per-device set-up: architecture check, acos table and the device angle's
+// distance from it, pool threshold.
 int device_setup(Device **out)
 {
     int dev = 0;
@@ -1234,6 +1336,7 @@ int device_setup(Device **out)
         if (hipMemcpy(d.table, t.data(), t.size() * sizeof(double), hipMemcpyHostToDevice) !=
             hipSuccess)
             return hip_fail();
+        d.slack = angle_slack(d.table);
         hipMemPool_t pool;
         if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
             uint64_t keep = UINT64_MAX;
@@ -1588,6 +1691,7 @@ Gate make_gate(const Device *d, const serac_params *p)
     G.table = d->table;
     G.max_ratio = p->max_ratio;
     G.max_distance = p->max_distance;
+    G.slack = d->slack;
     G.cross_check = p->cross_check;
     G.spin_limit = d->spin_limit;
     return G;
@@ -1751,8 +1855,13 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int
         launch_pair(J, p, descA, nA, descB, nB, w->aux + p.scratch, take_clear(w, p.acc),
                     params->cross_check != 0, stream);
         const Gate G = make_gate(d, params);
-        serac_finish_one<<<(nA + GATE_THREADS - 1) / GATE_THREADS, GATE_THREADS, 0, stream>>>(
-            J.rslot, J.nA, J.nB, J.Gc, J.cbest, G.table, G.cross_check, J, G);
+        const dim3 fg((nA + GATE_THREADS - 1) / GATE_THREADS);
+        if (J.cb32)
+            serac_finish_one<true><<<fg, GATE_THREADS, 0, stream>>>(
+                J.rslot, J.nA, J.nB, J.Gc, J.cbest, G.table, G.cross_check, J, G);
+        else
+            serac_finish_one<false><<<fg, GATE_THREADS, 0, stream>>>(
+                J.rslot, J.nA, J.nB, J.Gc, J.cbest, G.table, G.cross_check, J, G);
         if (hipGetLastError() != hipSuccess) {
             mark_dirty(w);
             return SERAC_ERR_HIP;
@@ -2106,6 +2215,20 @@ int serac_top2_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int3
             mark_dirty(w);
             return SERAC_ERR_HIP;
         }
+        return SERAC_OK;
+    });
+}
+
+int serac_angle_slack(double *slack)
+{
+    return guarded([&]() -> int {
+        if (!slack)
+            return SERAC_ERR_INVALID_ARG;
+        Device *d = nullptr;
+        const int st = device_setup(&d);
+        if (st != SERAC_OK)
+            return st;
+        *slack = d->slack;
         return SERAC_OK;
     });
 }

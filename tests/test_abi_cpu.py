@@ -25,7 +25,8 @@ def test_library_exports_every_declared_function():
     L = serac.library()
     names = declared() + declared(os.path.join(ROOT, "include", "serac_bench.h"))
     assert {"serac_match_pair", "serac_match_pairs", "serac_top2_pair",
-            "serac_status_string", "serac_profile_start", "serac_profile_stop"} <= set(names)
+            "serac_status_string", "serac_profile_start", "serac_profile_stop",
+            "serac_angle_slack"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
 
