@@ -61,6 +61,8 @@ extern "C" {
 #define SERAC_ERR_UNSUPPORTED_DEVICE (-3) /* current device is not gfx950 */
 #define SERAC_ERR_OUT_OF_MEMORY (-4)      /* device workspace allocation failed */
 #define SERAC_ERR_HIP (-5)                /* any other HIP runtime error */
+#define SERAC_ERR_TOO_LARGE (-6)          /* pair beyond serac_match_pair_noalloc's fixed scratch */
+#define SERAC_ERR_NOT_INITIALIZED (-7)    /* serac_match_pair_noalloc before the device's set-up */
 
 /* Largest descriptor count per image the library accepts. */
 #define SERAC_MAX_DESCRIPTORS 262144
@@ -122,6 +124,39 @@ typedef struct serac_pair {
 int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB,
                      int32_t nB, const serac_params *params,
                      const serac_matches *out_matches);
+
+/*
+ * Set up the current device for the library (architecture check, the angle
+ * table, the fixed scratch of serac_match_pair_noalloc): the work every
+ * other entry point does on its first call on a device, done now.  It
+ * allocates device memory.  Idempotent; after a transient failure the next
+ * call tries again.
+ * Errors: SERAC_ERR_UNSUPPORTED_DEVICE, SERAC_ERR_OUT_OF_MEMORY, SERAC_ERR_HIP.
+ */
+int serac_init(void);
+
+/*
+ * serac_match_pair for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, semantics and results as serac_match_pair; it
+ * makes no allocation and no free, and works in a fixed 4 MiB array of
+ * device memory that the library holds on each device until the process
+ * ends.  Each call leaves that array's accumulators zero again (a kernel at
+ * its end clears them), so a captured call can be replayed.  The device must
+ * have been set up first (serac_init, or any other entry point called on
+ * it), else SERAC_ERR_NOT_INITIALIZED.
+ * Limit: the single-kernel sweep (nA * nB <= 2^28) with a working set that
+ * fits the array: every pair of sets of up to 16384 descriptors does; nB
+ * above about 20000 does not.  Other pairs return SERAC_ERR_TOO_LARGE.
+ * All calls on one device share its array: calls that overlap on one
+ * device (two streams, or two threads on different streams) race and give
+ * wrong results; calls on one stream run in order.
+ * Errors: those of serac_match_pair, SERAC_ERR_TOO_LARGE,
+ * SERAC_ERR_NOT_INITIALIZED.
+ */
+int serac_match_pair_noalloc(const uint8_t *descA, int32_t nA, const uint8_t *descB,
+                             int32_t nB, const serac_params *params,
+                             const serac_matches *out_matches);
 
 /*
  * Match many pairs of one image set in one call, as exhaustive matching

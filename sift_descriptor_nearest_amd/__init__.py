@@ -12,6 +12,7 @@ import math
 import os
 
 __all__ = ["match_pair", "match_pair_into", "match_pairs", "match_pairs_host", "top2",
+           "init", "match_pair_noalloc_into",
            "profile_start", "profile_stop", "SeracError", "library", "LIB_PATH"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -24,6 +25,8 @@ SERAC_ERR_CAPACITY = -2
 SERAC_ERR_UNSUPPORTED_DEVICE = -3
 SERAC_ERR_OUT_OF_MEMORY = -4
 SERAC_ERR_HIP = -5
+SERAC_ERR_TOO_LARGE = -6
+SERAC_ERR_NOT_INITIALIZED = -7
 
 
 class serac_params(ctypes.Structure):
@@ -71,6 +74,8 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          ctypes.POINTER(serac_pair), i32,
                                          ctypes.POINTER(serac_params), i32,
                                          ctypes.POINTER(vp), ctypes.POINTER(i32)]
+    L.serac_match_pair_noalloc.argtypes = L.serac_match_pair.argtypes
+    L.serac_init.argtypes = []
     L.serac_top2_pair.argtypes = [vp, i32, vp, i32, vp, vp, vp]
     L.serac_profile_start.argtypes = [i32, i32]
     L.serac_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32),
@@ -81,7 +86,7 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.serac_status_string.argtypes = [ctypes.c_int]
     L.serac_status_string.restype = ctypes.c_char_p
     for f in (L.serac_match_pair, L.serac_match_pairs, L.serac_match_pairs_host,
-              L.serac_top2_pair,
+              L.serac_top2_pair, L.serac_init, L.serac_match_pair_noalloc,
               L.serac_profile_start, L.serac_profile_stop):
         f.restype = ctypes.c_int
     _lib = L
@@ -151,6 +156,36 @@ def match_pair_into(a, b, out, count, max_ratio=0.8, max_distance=math.inf,
                                     ctypes.byref(p), ctypes.byref(m))
     if rc != SERAC_OK:
         raise SeracError(rc, "serac_match_pair")
+
+
+def init(device=None) -> None:
+    """Set up `device` (default: the current one) for the library: what the
+    first call of any entry point on it would do, including the fixed
+    scratch of serac_match_pair_noalloc."""
+    import torch
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        rc = library().serac_init()
+    if rc != SERAC_OK:
+        raise SeracError(rc, "serac_init")
+
+
+def match_pair_noalloc_into(a, b, out, count, max_ratio=0.8, max_distance=math.inf,
+                            cross_check=True, stream=None) -> None:
+    """match_pair_into through serac_match_pair_noalloc: no device
+    allocation inside the library (the device must have been set up, e.g.
+    by init()).  Calls that overlap on one device race."""
+    _check_desc(a, "a")
+    _check_desc(b, "b")
+    if b.device != a.device:
+        raise ValueError("a and b must be on the same device")
+    _check_out(out, count, a.shape[0], a.device)
+    s = _stream(a.device) if stream is None else stream
+    p = _params(max_ratio, max_distance, cross_check, s)
+    m = serac_matches(out.data_ptr(), out.shape[0], count.data_ptr())
+    rc = library().serac_match_pair_noalloc(a.data_ptr(), a.shape[0], b.data_ptr(),
+                                            b.shape[0], ctypes.byref(p), ctypes.byref(m))
+    if rc != SERAC_OK:
+        raise SeracError(rc, "serac_match_pair_noalloc")
 
 
 def match_pair(a, b, max_ratio=0.8, max_distance=math.inf, cross_check=True):

@@ -1293,8 +1293,11 @@ double angle_slack(const double *table)
     return slack;
 }
 
+int fixed_setup(int dev);
+
 // Per-device set-up: architecture check, acos table and the device angle's
-// distance from it, pool threshold.
+// distance from it, the fixed scratch of the non-allocating entry point,
+// pool threshold.
 int device_setup(Device **out)
 {
     int dev = 0;
@@ -1337,6 +1340,8 @@ int device_setup(Device **out)
             hipSuccess)
             return hip_fail();
         d.slack = angle_slack(d.table);
+        if (const int st = fixed_setup(dev); st != SERAC_OK)
+            return st;
         hipMemPool_t pool;
         if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
             uint64_t keep = UINT64_MAX;
@@ -1348,6 +1353,22 @@ int device_setup(Device **out)
     }
     *out = &d;
     return d.status;
+}
+
+// The current device if it has been set up (no set-up work here), else null.
+Device *device_ready(int *dev_out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (dev < 0 || dev >= 64)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    Device &d = g_devices[dev];
+    *dev_out = dev;
+    return d.init && d.status == SERAC_OK ? &d : nullptr;
 }
 
 // Grow-only workspace per (device, stream).  Work on one stream runs in
@@ -1520,6 +1541,49 @@ Clear take_clear(Workspace *w, size_t leaves)
 void mark_dirty(Workspace *w)
 {
     w->dirty = true;
+}
+
+// ---- fixed scratch of serac_match_pair_noalloc
+//
+// One array per device, in the code object's device memory: the
+// accumulators (NOALLOC_REGION bytes; each call clears what it raised there
+// with a kernel at its end) and the per-call scratch after them.  It is
+// never allocated or freed; each device's copy lives at its own address,
+// taken once per device at set-up with hipGetSymbolAddress (the array's
+// name in host code is not a device address).  Every call on a device
+// shares that device's copy.  With 256 compute units every pair of sets of
+// up to 16384 descriptors fits (at most 2.1 MB of per-call scratch).
+constexpr size_t NOALLOC_REGION = 160u << 10;   // >= the accumulators of any accepted pair
+constexpr size_t NOALLOC_BYTES = 4u << 20;
+static __device__ __align__(256) uint8_t scratch[NOALLOC_BYTES];
+
+struct FixedScratch {
+    bool ready = false;
+    Workspace w;          // acc, aux point into this device's copy of `scratch`
+};
+FixedScratch g_fixed[64];
+
+// Set-up of device `dev`'s fixed scratch (under g_mutex, device current):
+// its address, and a clear by a kernel (its contents start at zero).  A
+// failure fails the device's set-up, which the next call then retries.
+int fixed_setup(int dev)
+{
+    FixedScratch &f = g_fixed[dev];
+    if (f.ready)
+        return SERAC_OK;
+    uint8_t *ptr = nullptr;
+    if (hipGetSymbolAddress((void **)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+        return hip_fail();
+    serac_clear<<<256, 256>>>(reinterpret_cast<uint4 *>(ptr), NOALLOC_BYTES / 16);
+    if (hipGetLastError() != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+        return hip_fail();
+    f.w.dev = dev;
+    f.w.acc = ptr;
+    f.w.acc_bytes = NOALLOC_REGION;
+    f.w.aux = f.w.acc + NOALLOC_REGION;
+    f.w.aux_bytes = NOALLOC_BYTES - NOALLOC_REGION;
+    f.ready = true;
+    return SERAC_OK;
 }
 
 struct Plan {
@@ -1785,6 +1849,54 @@ void launch_pair(Job &J, const Plan &p, const uint8_t *A, int nA, const uint8_t 
     launch_tiles(J, p, cols, stream);
 }
 
+// The kernels of one pair (nA, nB > 0) on `stream`, with w's accumulators
+// and w's scratch (p.scratch, then the prepared sets): the sweep (after the
+// preparation kernel for a large pair) and the finishing kernel.  The caller
+// holds w's lock and has sized w for p.
+// Accumulators: by default the call takes w's next region and its first
+// kernel clears what the previous call left in the other one (host-side
+// bookkeeping).  With `self_clear` it always takes the first region and a
+// kernel after the finishing kernel clears what this call raised there, so
+// the region is zero whenever a call starts without the host tracking
+// anything, also when a captured graph of the call is replayed.
+int enqueue_pair(const Device *d, const Plan &p, Workspace *w, const uint8_t *A, int nA,
+                 const uint8_t *B, int nB, const serac_params *params, const serac_matches *out,
+                 hipStream_t stream, bool self_clear = false)
+{
+    if (w->dirty) {
+        serac_clear<<<1024, 256, 0, stream>>>(reinterpret_cast<uint4 *>(w->acc), w->acc_bytes / 16);
+        if (hipGetLastError() != hipSuccess)
+            return SERAC_ERR_HIP;
+        w->dirty = false;
+        w->acc_used[0] = w->acc_used[1] = 0;
+    }
+    Job J;
+    const PrepJob none{};
+    uint8_t *const region = self_clear ? w->acc : next_region(w);
+    fill_job(J, p, A, nA, none, B, nB, none, region, w->aux, out->matches, out->count);
+    const Clear C = self_clear ? Clear{reinterpret_cast<uint4 *>(w->acc), 0, 1}
+                               : take_clear(w, p.acc);
+    launch_pair(J, p, A, nA, B, nB, w->aux + p.scratch, C, params->cross_check != 0, stream);
+    const Gate G = make_gate(d, params);
+    const dim3 fg((nA + GATE_THREADS - 1) / GATE_THREADS);
+    if (J.cb32)
+        serac_finish_one<true><<<fg, GATE_THREADS, 0, stream>>>(
+            J.rslot, J.nA, J.nB, J.Gc, J.cbest, G.table, G.cross_check, J, G);
+    else
+        serac_finish_one<false><<<fg, GATE_THREADS, 0, stream>>>(
+            J.rslot, J.nA, J.nB, J.Gc, J.cbest, G.table, G.cross_check, J, G);
+    if (self_clear) {
+        const size_t words = p.acc / 16;
+        serac_clear<<<(unsigned)std::min<size_t>((words + 255) / 256, 1024), 256, 0, stream>>>(
+            reinterpret_cast<uint4 *>(region), words);
+    }
+    if (hipGetLastError() != hipSuccess) {
+        mark_dirty(w);
+        return SERAC_ERR_HIP;
+    }
+    return SERAC_OK;
+}
+
 // Runs an entry point's body: no C++ exception crosses the C interface (a
 // failed host allocation is reported as out of memory, anything else as a
 // runtime error).
@@ -1819,6 +1931,10 @@ const char *serac_status_string(int status)
         return "device memory allocation failed";
     case SERAC_ERR_HIP:
         return "HIP runtime error";
+    case SERAC_ERR_TOO_LARGE:
+        return "pair too large for the fixed scratch of the non-allocating entry point";
+    case SERAC_ERR_NOT_INITIALIZED:
+        return "device not set up (call serac_init first)";
     default:
         return "unknown status";
     }
@@ -1848,25 +1964,46 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int
         st = get_workspace(stream, p.acc, p.scratch + pair_prep_bytes(nA, nB), &w, hold);
         if (st != SERAC_OK)
             return st;
-        Job J;
-        const PrepJob none{};
-        fill_job(J, p, descA, nA, none, descB, nB, none, next_region(w), w->aux, out->matches,
-                 out->count);
-        launch_pair(J, p, descA, nA, descB, nB, w->aux + p.scratch, take_clear(w, p.acc),
-                    params->cross_check != 0, stream);
-        const Gate G = make_gate(d, params);
-        const dim3 fg((nA + GATE_THREADS - 1) / GATE_THREADS);
-        if (J.cb32)
-            serac_finish_one<true><<<fg, GATE_THREADS, 0, stream>>>(
-                J.rslot, J.nA, J.nB, J.Gc, J.cbest, G.table, G.cross_check, J, G);
-        else
-            serac_finish_one<false><<<fg, GATE_THREADS, 0, stream>>>(
-                J.rslot, J.nA, J.nB, J.Gc, J.cbest, G.table, G.cross_check, J, G);
-        if (hipGetLastError() != hipSuccess) {
-            mark_dirty(w);
-            return SERAC_ERR_HIP;
+        return enqueue_pair(d, p, w, descA, nA, descB, nB, params, out, stream);
+    });
+}
+
+int serac_init(void)
+{
+    return guarded([&]() -> int {
+        Device *d = nullptr;
+        return device_setup(&d);
+    });
+}
+
+int serac_match_pair_noalloc(const uint8_t *descA, int32_t nA, const uint8_t *descB, int32_t nB,
+                             const serac_params *params, const serac_matches *out)
+{
+    return guarded([&]() -> int {
+        if (bad_set(descA, nA) || bad_set(descB, nB) || bad_params(params) || !out ||
+            bad_out(*out, nA))
+            return SERAC_ERR_INVALID_ARG;
+        if (out->capacity < nA)
+            return SERAC_ERR_CAPACITY;
+        if (!fused_pair(nA, nB))
+            return SERAC_ERR_TOO_LARGE;
+        int dev = 0;
+        Device *d = device_ready(&dev);
+        if (!d)
+            return SERAC_ERR_NOT_INITIALIZED;
+        FixedScratch &f = g_fixed[dev];
+        if (!f.ready)
+            return SERAC_ERR_NOT_INITIALIZED;
+        hipStream_t stream = static_cast<hipStream_t>(params->stream);
+        if (nA == 0 || nB == 0) {
+            serac_zero_counts<<<1, 64, 0, stream>>>(nullptr, out->count, 1);
+            return hipGetLastError() == hipSuccess ? SERAC_OK : SERAC_ERR_HIP;
         }
-        return SERAC_OK;
+        const Plan p = make_plan(nA, nB, 0, d->cus);
+        if (p.acc > NOALLOC_REGION || p.scratch > f.w.aux_bytes)
+            return SERAC_ERR_TOO_LARGE;
+        std::lock_guard<std::mutex> hold(f.w.busy);
+        return enqueue_pair(d, p, &f.w, descA, nA, descB, nB, params, out, stream, true);
     });
 }
 

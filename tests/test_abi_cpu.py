@@ -25,7 +25,7 @@ def test_library_exports_every_declared_function():
     L = serac.library()
     names = declared() + declared(os.path.join(ROOT, "include", "serac_bench.h"))
     assert {"serac_match_pair", "serac_match_pairs", "serac_top2_pair",
-            "serac_status_string", "serac_profile_start", "serac_profile_stop",
+            "serac_init", "serac_match_pair_noalloc", "serac_status_string", "serac_profile_start", "serac_profile_stop",
             "serac_angle_slack"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
@@ -46,7 +46,7 @@ def test_every_header_is_checked():
 
 def test_status_strings():
     L = serac.library()
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert L.serac_status_string(st)
     assert L.serac_status_string(12345) == b"unknown status"
 
@@ -104,6 +104,32 @@ def test_match_pair_rejects_misaligned_pointers():
     L = serac.library()
     assert L.serac_top2_pair(FAKE, 3, FAKE, 3, None, FAKE + 2, FAKE) == E
     assert L.serac_top2_pair(FAKE, 3, FAKE, 3, None, FAKE, FAKE + 1) == E
+
+
+def test_match_pair_noalloc_validation():
+    """The non-allocating entry point validates as serac_match_pair does and
+    refuses, before any HIP call, a pair beyond its single-kernel limit."""
+    L = serac.library()
+    E = serac.SERAC_ERR_INVALID_ARG
+
+    def call(a=FAKE, nA=10, b=FAKE, nB=10, params=None, out=None):
+        pp = ctypes.byref(params or _p())
+        oo = ctypes.byref(out or _m())
+        return L.serac_match_pair_noalloc(a, nA, b, nB, pp, oo)
+
+    assert call(a=None) == E
+    assert call(b=FAKE + 8) == E
+    assert call(nA=-1) == E
+    assert call(params=_p(flags=1)) == E
+    assert call(params=_p(max_ratio=0.0)) == E
+    assert call(out=serac_matches(FAKE + 4, 100, FAKE)) == E
+    assert L.serac_match_pair_noalloc(FAKE, 10, FAKE, 10, None, ctypes.byref(_m())) == E
+    assert L.serac_match_pair_noalloc(FAKE, 10, FAKE, 10, ctypes.byref(_p()), None) == E
+    assert call(nA=101) == serac.SERAC_ERR_CAPACITY
+    big = serac_matches(FAKE, 1 << 20, FAKE)
+    assert call(nA=16385, nB=16385, out=big) == serac.SERAC_ERR_TOO_LARGE
+    assert call(nA=1, nB=(1 << 28) + 1, out=big) == serac.SERAC_ERR_INVALID_ARG   # > max set
+    assert call(nA=2048, nB=131073, out=big) == serac.SERAC_ERR_TOO_LARGE
 
 
 def test_match_pair_rejects_small_capacity():
