@@ -51,9 +51,12 @@ def load(path: str = LIB) -> ctypes.CDLL:
     lib.oracle_match_pair.argtypes = [u8p, i32, u8p, i32, ctypes.c_double,
                                       ctypes.c_double, i32, u32p, i32p,
                                       ctypes.c_int]
+    lib.oracle_match_pair_sym.argtypes = [u8p, i32, u8p, i32, ctypes.c_double,
+                                          ctypes.c_double, u32p, i32p, ctypes.c_int]
     lib.oracle_max_threads.argtypes = []
     for f in (lib.oracle_top2, lib.oracle_rows, lib.oracle_cols,
-              lib.oracle_accept, lib.oracle_match_pair, lib.oracle_max_threads):
+              lib.oracle_accept, lib.oracle_match_pair, lib.oracle_match_pair_sym,
+              lib.oracle_max_threads):
         f.restype = ctypes.c_int
     return lib
 
@@ -136,18 +139,39 @@ def accept(i, best, idx, second, colidx_of_best, max_ratio=0.8,
                                           int(bool(cross_check))))
 
 
+def cap(X, max_features: int = 0) -> np.ndarray:
+    """The match cap: only the first max_features descriptors of an image
+    take part (0: no cap).  The SERAC README ("Memory") describes lowering
+    COLMAP's cap as clamping the lower-scale features away, i.e. features
+    are kept in their stored order, largest scale first, up to the cap."""
+    if max_features < 0:
+        raise ValueError("max_features must be >= 0")
+    return X[:max_features] if max_features else X
+
+
 def match_pair(A, B, max_ratio=0.8, max_distance=float("inf"),
-               cross_check=True, nthreads: int = 0, L=None) -> np.ndarray:
-    """Accepted correspondences, uint32 [count, 2] = (row of A, row of B)."""
+               cross_check=True, nthreads: int = 0, L=None, symmetric=False,
+               max_features: int = 0) -> np.ndarray:
+    """Accepted correspondences, uint32 [count, 2] = (row of A, row of B).
+
+    symmetric: the column side passes the same gates (serac_oracle.c,
+    "symmetric"); it implies the cross-check.  max_features: the match cap
+    (see cap())."""
     L = L or lib()
-    A, B = _u8(A), _u8(B)
+    A, B = _u8(cap(A, max_features)), _u8(cap(B, max_features))
     out = np.zeros((max(A.shape[0], 1), 2), dtype=np.uint32)
     cnt = ctypes.c_int32(0)
-    rc = L.oracle_match_pair(_p(A, ctypes.c_uint8), A.shape[0],
-                             _p(B, ctypes.c_uint8), B.shape[0],
-                             float(max_ratio), float(max_distance),
-                             int(bool(cross_check)), _p(out, ctypes.c_uint32),
-                             ctypes.byref(cnt), nthreads)
+    if symmetric:
+        rc = L.oracle_match_pair_sym(_p(A, ctypes.c_uint8), A.shape[0],
+                                     _p(B, ctypes.c_uint8), B.shape[0],
+                                     float(max_ratio), float(max_distance),
+                                     _p(out, ctypes.c_uint32), ctypes.byref(cnt), nthreads)
+    else:
+        rc = L.oracle_match_pair(_p(A, ctypes.c_uint8), A.shape[0],
+                                 _p(B, ctypes.c_uint8), B.shape[0],
+                                 float(max_ratio), float(max_distance),
+                                 int(bool(cross_check)), _p(out, ctypes.c_uint32),
+                                 ctypes.byref(cnt), nthreads)
     if rc:
         raise RuntimeError("oracle_match_pair failed")
     return out[:cnt.value].copy()

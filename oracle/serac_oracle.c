@@ -30,6 +30,14 @@
  *   output   (i, idx) as two little-endian uint32 per accepted row, rows in
  *            ascending order; the README stores one correspondence blob per
  *            pair of about 8 bytes per correspondence.
+ *   symmetric (an option the pages do not define; the plainest reading of
+ *            "symmetric column gates"): the column side passes the same
+ *            gates as the row side.  Column j's (best, idx, second) is its
+ *            scan over ascending i with the row rules (ties to the lowest
+ *            row, second with multiplicity), i.e. row j of the scores of the
+ *            swapped pair (B, A).  Row i with idx = j >= 0 is accepted iff
+ *            row i passes the gates, column j passes them on its own best
+ *            and second, and column j's idx is i (the cross-check).
  *
  * Everything is in int32 / IEEE double with no fast-math and no FMA
  * contraction (built with -O2 -ffp-contract=off).  The scores are computed
@@ -240,6 +248,54 @@ int oracle_accept(int32_t i, int32_t best, int32_t idx, int32_t second,
     if (cross_check && colidx_of_best != i)
         return 0;
     return 1;
+}
+
+/*
+ * The matcher with symmetric column gates (header: "symmetric").  The
+ * column top-2 is the row top-2 of the swapped pair: S(B, A)[j][i] =
+ * S(A, B)[i][j], scanned over ascending i.  out_pairs has room for nA
+ * pairs; *count receives the number written.  Returns 0 or -1.
+ */
+int oracle_match_pair_sym(const uint8_t *A, int32_t nA, const uint8_t *B,
+                          int32_t nB, double max_ratio, double max_distance,
+                          uint32_t *out_pairs, int32_t *count, int nthreads)
+{
+    if (!count || nA < 0 || nB < 0 || (nA > 0 && !out_pairs))
+        return -1;
+    *count = 0;
+    if (nA == 0 || nB == 0)
+        return 0;
+    int32_t *row = (int32_t *)malloc((size_t)nA * 3 * sizeof(int32_t));
+    int32_t *col = (int32_t *)malloc((size_t)nB * 3 * sizeof(int32_t));
+    if (!row || !col) {
+        free(row);
+        free(col);
+        return -1;
+    }
+    int rc = oracle_top2(A, nA, B, nB, row, NULL, nthreads);
+    if (rc == 0)
+        rc = oracle_top2(B, nB, A, nA, col, NULL, nthreads);
+    if (rc == 0) {
+        int32_t n = 0;
+        for (int32_t i = 0; i < nA; ++i) {
+            int32_t best = row[3 * i], j = row[3 * i + 1], second = row[3 * i + 2];
+            if (!oracle_accept(i, best, j, second, -1, max_ratio, max_distance, 0))
+                continue;
+            /* column j: its own best row, best score and second */
+            int32_t cbest = col[3 * j], ci = col[3 * j + 1], csecond = col[3 * j + 2];
+            if (ci != i)
+                continue;
+            if (!oracle_accept(j, cbest, ci, csecond, -1, max_ratio, max_distance, 0))
+                continue;
+            out_pairs[2 * n] = (uint32_t)i;
+            out_pairs[2 * n + 1] = (uint32_t)j;
+            ++n;
+        }
+        *count = n;
+    }
+    free(row);
+    free(col);
+    return rc;
 }
 
 /*

@@ -22,6 +22,7 @@ from __future__ import annotations
 import json
 import math
 import os
+from types import SimpleNamespace
 
 import numpy as np
 
@@ -217,6 +218,8 @@ def golden_cases():
         if fn.endswith(".json"):
             with open(os.path.join(GOLDEN, fn)) as f:
                 doc = json.load(f)
+            if "cases" not in doc:          # the oracle's digests, not a fixture
+                continue
             for case in doc["cases"]:
                 out.append((fn, case))
     return out
@@ -233,7 +236,9 @@ def pin_golden(L):
         assert col.tolist() == c["col_best"], (fn, c["name"], "col")
         p = c["params"]
         md = math.inf if p["max_distance"] is None else p["max_distance"]
-        got = oracle.match_pair(A, B, p["max_ratio"], md, p["cross_check"], L=L)
+        got = oracle.match_pair(A, B, p["max_ratio"], md, p["cross_check"], L=L,
+                                symmetric=p.get("symmetric", False),
+                                max_features=p.get("max_features", 0))
         assert got.tolist() == c["matches"], (fn, c["name"], "matches")
 
 
@@ -264,5 +269,71 @@ def pin_invariants(L):
     assert len(ties) > 0 and not set(ties.tolist()) & set(got[:, 0].tolist())
 
 
+def brute_symmetric(A, B, max_ratio, max_distance):
+    """Symmetric column gates from the brute-force top-2 of (A, B) and of
+    the swapped pair (B, A): row gates, column gates, mutual best."""
+    row, _ = brute_top2(A, B)
+    colT, _ = brute_top2(B, A)
+    rows = brute_matches(row, None, max_ratio, max_distance, False).tolist()
+    cols = {j: i for j, i in brute_matches(colT, None, max_ratio, max_distance,
+                                           False).tolist()}
+    out = [(i, j) for i, j in rows if cols.get(j) == i]
+    return np.array(out, dtype=np.uint32).reshape(-1, 2)
+
+
+def pin_symmetric(L):
+    """Symmetric column gates: brute force on tiny tie-heavy pairs; swapping
+    the two sets transposes the list; it is the cross-checked list of (A, B)
+    intersected with the transposed cross-checked list of (B, A); and on
+    clean planted pairs it drops nothing the cross-check keeps."""
+    rng = np.random.default_rng(99)
+    for nA, nB in ((0, 5), (5, 0), (1, 1), (3, 17), (17, 3), (40, 33)):
+        A, B = tie_heavy(rng, nA), tie_heavy(rng, nB)
+        for r in (0.8, 1.0, 1.5):
+            got = oracle.match_pair(A, B, r, math.inf, True, L=L, symmetric=True)
+            assert np.array_equal(got, brute_symmetric(A, B, r, math.inf)), (nA, nB, r)
+    cases = [synth.edge_pair(500, 450, 120, 40, False, 3), synth.pair(700, 650, 0.3, 6, 4)]
+    A, B = tie_heavy(rng, 300), tie_heavy(rng, 280)
+    for p in cases + [SimpleNamespace(A=A, B=B)]:
+        for r, md in ((0.8, math.inf), (0.95, 0.7), (1.3, math.inf)):
+            fwd = oracle.match_pair(p.A, p.B, r, md, True, L=L, symmetric=True)
+            rev = oracle.match_pair(p.B, p.A, r, md, True, L=L, symmetric=True)
+            f = {tuple(x) for x in fwd.tolist()}
+            assert f == {(b, a) for a, b in rev.tolist()}, ("swap", r, md)
+            c1 = {tuple(x) for x in oracle.match_pair(p.A, p.B, r, md, True, L=L).tolist()}
+            c2 = {(b, a) for a, b in oracle.match_pair(p.B, p.A, r, md, True, L=L).tolist()}
+            assert f == c1 & c2, ("intersection", r, md)
+            assert np.all(np.diff(fwd[:, 0].astype(np.int64)) > 0)
+    q = synth.pair(1000, 1200, 0.3, 3, 0)
+    sym = oracle.match_pair(q.A, q.B, 0.8, math.inf, True, L=L, symmetric=True)
+    assert {tuple(t) for t in sym.astype(np.int64).tolist()} == \
+        {tuple(t) for t in q.truth.tolist()}
+
+
+def pin_cap(L):
+    """The match cap: no cap (0) and a cap at or above both sizes change
+    nothing; a cap K matches exactly the pair of the first K rows of each
+    set (brute force on tiny pairs), so every index is below K."""
+    rng = np.random.default_rng(5)
+    p = synth.pair(300, 260, 0.3, 4, 1)
+    full = oracle.match_pair(p.A, p.B, L=L)
+    assert np.array_equal(oracle.match_pair(p.A, p.B, L=L, max_features=0), full)
+    assert np.array_equal(oracle.match_pair(p.A, p.B, L=L, max_features=300), full)
+    for K in (1, 100, 259):
+        got = oracle.match_pair(p.A, p.B, L=L, max_features=K)
+        assert got.size == 0 or got.max() < K
+    for K in (1, 4, 9):
+        A, B = tie_heavy(rng, 12), tie_heavy(rng, 10)
+        row, col = brute_top2(A[:K], B[:K])
+        for r in (0.8, 1.5):
+            want = brute_matches(row, col, r, math.inf, True)
+            got = oracle.match_pair(A, B, r, math.inf, True, L=L, max_features=K)
+            assert np.array_equal(got, want), (K, r)
+            sym = oracle.match_pair(A, B, r, math.inf, True, L=L, max_features=K,
+                                    symmetric=True)
+            assert np.array_equal(sym, brute_symmetric(A[:K], B[:K], r, math.inf)), (K, r)
+
+
 PINS = [pin_brute_tiny, pin_numpy_scores, pin_closed_forms,
-        pin_gate_closed_cases, pin_golden, pin_planted, pin_invariants]
+        pin_gate_closed_cases, pin_golden, pin_planted, pin_invariants,
+        pin_symmetric, pin_cap]

@@ -34,6 +34,11 @@ MUTANTS = {
     "cosine_wrong_norm": ("(double)s / (double)NORM2", "(double)s / 262143.0"),
     "cosine_not_clamped": ("(s >= NORM2) ? 1.0 :", "0 ? 1.0 :"),
     "cross_check_ignored": ("if (cross_check && colidx_of_best != i)", "if (0)"),
+    "sym_column_gate_dropped": (
+        "if (!oracle_accept(j, cbest, ci, csecond, -1, max_ratio, max_distance, 0))",
+        "if (0)"),
+    "sym_mutual_check_dropped": ("if (ci != i)\n                continue;", "if (0)\n                continue;"),
+    "sym_column_second_from_row": ("csecond = col[3 * j + 2];", "csecond = second;"),
 }
 
 
