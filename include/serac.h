@@ -57,7 +57,7 @@ extern "C" {
 /* Status codes. */
 #define SERAC_OK 0
 #define SERAC_ERR_INVALID_ARG (-1)        /* NULL with n > 0, n < 0, n too large, bad params */
-#define SERAC_ERR_CAPACITY (-2)           /* output capacity smaller than nA */
+#define SERAC_ERR_CAPACITY (-2)           /* output capacity smaller than nA (after the cap) */
 #define SERAC_ERR_UNSUPPORTED_DEVICE (-3) /* current device is not gfx950 */
 #define SERAC_ERR_OUT_OF_MEMORY (-4)      /* device workspace allocation failed */
 #define SERAC_ERR_HIP (-5)                /* any other HIP runtime error */
@@ -75,15 +75,38 @@ extern "C" {
  *                disables the gate; NaN is an error.
  *   cross_check  0 or 1: require row i to be the best row of its best
  *                column (lowest row on a tie).
- *   flags        reserved, must be 0.
- *   stream       hipStream_t to enqueue on; NULL selects the null stream. */
+ *   flags        0, or SERAC_FLAG_SYMMETRIC; other bits are an error.
+ *   stream       hipStream_t to enqueue on; NULL selects the null stream.
+ *   max_features the match cap: when > 0, only the first max_features
+ *                descriptors of each set take part (the rest are ignored,
+ *                as if the sets were that long; output indices are
+ *                unchanged).  The SERAC README ("Memory") describes
+ *                lowering COLMAP's cap as clamping the lower-scale features
+ *                away, i.e. features stored largest scale first are kept up
+ *                to the cap.  0: no cap; negative is an error.  Output
+ *                capacity is then needed for min(nA, max_features) rows.
+ *   reserved     must be 0. */
 typedef struct serac_params {
     double max_ratio;
     double max_distance;
     int32_t cross_check;
     int32_t flags;
     void *stream;
+    int32_t max_features;
+    int32_t reserved;
 } serac_params;
+
+/* Symmetric column gates (an option the pages name without defining it;
+ * this is its plainest reading): column j must pass the same gates as row
+ * i, on its own best and second-best score over all rows (lowest row on a
+ * tie, second counted with multiplicity), and the two must be each other's
+ * best:
+ *   accept (i, j) iff row i passes, j = idx_i, col j passes, col_idx[j] == i.
+ * It implies the cross-check (cross_check is then ignored).  The library
+ * runs it as two sweeps, of (A, B) and of (B, A), without column bests: about
+ * twice the work of one call.  serac_match_pair and serac_match_pairs take
+ * it; serac_match_pair_noalloc refuses it (SERAC_ERR_INVALID_ARG). */
+#define SERAC_FLAG_SYMMETRIC 1
 
 /* One correspondence: row a of the first set, row b of the second. */
 typedef struct serac_match {
@@ -97,8 +120,9 @@ typedef struct serac_match {
  * complete (a bounded wait that only a malfunctioning device exhausts; the
  * match list is then invalid).  The bound is 2^22 polls; for tests, the
  * environment variable SERAC_LOOKBACK_SPIN_LIMIT read at the first call on
- * a device replaces it (-1: give up at once).  capacity must be at least nA
- * (each row yields at most one match). */
+ * a device replaces it (-1: give up at once).  capacity must be at least nA,
+ * or min(nA, max_features) under a match cap (each row yields at most one
+ * match). */
 typedef struct serac_matches {
     serac_match *matches;
     int64_t capacity;
@@ -166,7 +190,7 @@ int serac_match_pair_noalloc(const uint8_t *descA, int32_t nA, const uint8_t *de
  *   n         host array [num_images] of descriptor counts
  *   pairs     host array [num_pairs] of image index pairs (a, b)
  *   out_matches host array [num_pairs]; out_matches[p] receives pair p's
- *             matches (capacity >= n[pairs[p].a]).
+ *             matches (capacity >= n[pairs[p].a], or the cap if smaller).
  * Every pair gets exactly the result serac_match_pair would give it.
  * Asynchronous on params->stream like the other entry points: the host
  * arrays are read before the call returns (they may be released at once);

@@ -27,12 +27,14 @@ SERAC_ERR_OUT_OF_MEMORY = -4
 SERAC_ERR_HIP = -5
 SERAC_ERR_TOO_LARGE = -6
 SERAC_ERR_NOT_INITIALIZED = -7
+SERAC_FLAG_SYMMETRIC = 1
 
 
 class serac_params(ctypes.Structure):
     _fields_ = [("max_ratio", ctypes.c_double), ("max_distance", ctypes.c_double),
                 ("cross_check", ctypes.c_int32), ("flags", ctypes.c_int32),
-                ("stream", ctypes.c_void_p)]
+                ("stream", ctypes.c_void_p), ("max_features", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class serac_matches(ctypes.Structure):
@@ -120,9 +122,14 @@ def _check_out(out, count, nA, device):
         raise ValueError("out must be 8-byte aligned and count 4-byte aligned")
 
 
-def _params(max_ratio, max_distance, cross_check, stream):
+def _params(max_ratio, max_distance, cross_check, stream, symmetric=False, max_features=0):
     return serac_params(float(max_ratio), float(max_distance), int(bool(cross_check)),
-                        0, ctypes.c_void_p(stream))
+                        SERAC_FLAG_SYMMETRIC if symmetric else 0, ctypes.c_void_p(stream),
+                        int(max_features), 0)
+
+
+def _capped(n, max_features):
+    return min(n, max_features) if max_features > 0 else n
 
 
 def _stream(device):
@@ -138,19 +145,21 @@ def _stream(device):
 
 
 def match_pair_into(a, b, out, count, max_ratio=0.8, max_distance=math.inf,
-                    cross_check=True, stream=None) -> None:
+                    cross_check=True, stream=None, symmetric=False, max_features=0) -> None:
     """Enqueue one pair; out is int32 [>= nA, 2], count int32 [1] (device).
 
     Asynchronous on the current stream (or ``stream``, a raw hipStream_t);
-    nothing is synchronised.
+    nothing is synchronised.  symmetric: the column side passes the same
+    gates (SERAC_FLAG_SYMMETRIC); max_features: the match cap (only the
+    first max_features rows of each set take part; 0 = none).
     """
     _check_desc(a, "a")
     _check_desc(b, "b")
     if b.device != a.device:
         raise ValueError("a and b must be on the same device")
-    _check_out(out, count, a.shape[0], a.device)
+    _check_out(out, count, _capped(a.shape[0], max_features), a.device)
     s = _stream(a.device) if stream is None else stream
-    p = _params(max_ratio, max_distance, cross_check, s)
+    p = _params(max_ratio, max_distance, cross_check, s, symmetric, max_features)
     m = serac_matches(out.data_ptr(), out.shape[0], count.data_ptr())
     rc = library().serac_match_pair(a.data_ptr(), a.shape[0], b.data_ptr(), b.shape[0],
                                     ctypes.byref(p), ctypes.byref(m))
@@ -170,7 +179,7 @@ def init(device=None) -> None:
 
 
 def match_pair_noalloc_into(a, b, out, count, max_ratio=0.8, max_distance=math.inf,
-                            cross_check=True, stream=None) -> None:
+                            cross_check=True, stream=None, max_features=0) -> None:
     """match_pair_into through serac_match_pair_noalloc: no device
     allocation inside the library (the device must have been set up, e.g.
     by init()).  Calls that overlap on one device race."""
@@ -178,9 +187,9 @@ def match_pair_noalloc_into(a, b, out, count, max_ratio=0.8, max_distance=math.i
     _check_desc(b, "b")
     if b.device != a.device:
         raise ValueError("a and b must be on the same device")
-    _check_out(out, count, a.shape[0], a.device)
+    _check_out(out, count, _capped(a.shape[0], max_features), a.device)
     s = _stream(a.device) if stream is None else stream
-    p = _params(max_ratio, max_distance, cross_check, s)
+    p = _params(max_ratio, max_distance, cross_check, s, False, max_features)
     m = serac_matches(out.data_ptr(), out.shape[0], count.data_ptr())
     rc = library().serac_match_pair_noalloc(a.data_ptr(), a.shape[0], b.data_ptr(),
                                             b.shape[0], ctypes.byref(p), ctypes.byref(m))
@@ -188,7 +197,8 @@ def match_pair_noalloc_into(a, b, out, count, max_ratio=0.8, max_distance=math.i
         raise SeracError(rc, "serac_match_pair_noalloc")
 
 
-def match_pair(a, b, max_ratio=0.8, max_distance=math.inf, cross_check=True):
+def match_pair(a, b, max_ratio=0.8, max_distance=math.inf, cross_check=True,
+               symmetric=False, max_features=0):
     """Matches of one pair as int32 [count, 2] = (row of a, row of b).
 
     Synchronises the stream to read the count.
@@ -196,7 +206,8 @@ def match_pair(a, b, max_ratio=0.8, max_distance=math.inf, cross_check=True):
     import torch
     out = torch.empty((max(a.shape[0], 1), 2), dtype=torch.int32, device=a.device)
     count = torch.empty(1, dtype=torch.int32, device=a.device)
-    match_pair_into(a, b, out, count, max_ratio, max_distance, cross_check)
+    match_pair_into(a, b, out, count, max_ratio, max_distance, cross_check,
+                    symmetric=symmetric, max_features=max_features)
     n = int(count.item())
     if n < 0:
         raise SeracError(SERAC_ERR_HIP, "serac_match_pair: ordered output hand-off failed")
@@ -204,7 +215,7 @@ def match_pair(a, b, max_ratio=0.8, max_distance=math.inf, cross_check=True):
 
 
 def match_pairs(images, pairs, max_ratio=0.8, max_distance=math.inf,
-                cross_check=True):
+                cross_check=True, symmetric=False, max_features=0):
     """Match many pairs of one image set in one call.
 
     images: list of uint8 CUDA tensors [n_k, 128] on one device;
@@ -238,7 +249,7 @@ def match_pairs(images, pairs, max_ratio=0.8, max_distance=math.inf,
     ms["matches"] = out.data_ptr() + offs[:-1] * 8
     ms["capacity"] = caps
     ms["count"] = counts.data_ptr() + 4 * np.arange(P, dtype=np.uint64)
-    prm = _params(max_ratio, max_distance, cross_check, _stream(dev))
+    prm = _params(max_ratio, max_distance, cross_check, _stream(dev), symmetric, max_features)
     rc = library().serac_match_pairs(ptrs, ns.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                                      len(images), cp.ctypes.data_as(ctypes.POINTER(serac_pair)),
                                      P, ctypes.byref(prm),
@@ -257,7 +268,7 @@ def match_pairs(images, pairs, max_ratio=0.8, max_distance=math.inf,
 
 
 def match_pairs_host(images, pairs, max_ratio=0.8, max_distance=math.inf,
-                     cross_check=True, pairs_per_stage=0):
+                     cross_check=True, pairs_per_stage=0, symmetric=False, max_features=0):
     """Match many pairs and return the match lists in host memory.
 
     Same inputs and results as match_pairs, but the lists arrive as numpy
@@ -286,7 +297,8 @@ def match_pairs_host(images, pairs, max_ratio=0.8, max_distance=math.inf,
     ns = nimg.astype(np.int32)
     cp = np.ascontiguousarray(pr.astype(np.int32))          # serac_pair [P]
     hp = (host.ctypes.data + offs[:-1] * 8).astype(np.uint64)
-    prm = _params(max_ratio, max_distance, cross_check, _stream(images[0].device))
+    prm = _params(max_ratio, max_distance, cross_check, _stream(images[0].device), symmetric,
+                  max_features)
     rc = library().serac_match_pairs_host(
         ptrs, ns.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(images),
         cp.ctypes.data_as(ctypes.POINTER(serac_pair)), P, ctypes.byref(prm),

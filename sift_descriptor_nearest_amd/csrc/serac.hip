@@ -85,6 +85,12 @@
 #include "serac.h"
 #include "serac_bench.h"
 
+#include <cstddef>
+
+static_assert(sizeof(serac_params) == 40 && offsetof(serac_params, stream) == 24 &&
+                  offsetof(serac_params, max_features) == 32,
+              "serac_params layout (the Python binding mirrors it)");
+
 namespace {
 
 constexpr int DIM = 128;
@@ -933,8 +939,20 @@ __device__ __forceinline__ void status_store(unsigned long long *p, unsigned lon
 // where it settles them (gates_sure), computed while the column best of the
 // row's best column is being loaded, so that the table is read only for the
 // rare row the device angle leaves open.
-template <bool DEV_ANGLE, bool NARROW = false>
-__device__ __forceinline__ void finish_body(const Job &J, int wg, int nwg, const Gate &G)
+//
+// SYM: symmetric column gates, in two passes over two sweeps without column
+// bests.  SYM_COLUMNS finishes the sweep of the swapped pair (B, A): row r
+// of it is column r of the pair, and the kernel writes, densely, the row of
+// A that column r accepts under the gates (its best row, lowest on a tie),
+// or -1, into that sweep's rs1 (which only the top-2 export uses
+// otherwise).  SYM_ROWS finishes the sweep of (A, B): row i passes if it
+// passes the gates and its best column accepts exactly row i, which is the
+// mutual check and the column's own gates in one comparison.
+constexpr int SYM_NONE = 0, SYM_COLUMNS = 1, SYM_ROWS = 2;
+
+template <bool DEV_ANGLE, bool NARROW = false, int SYM = SYM_NONE>
+__device__ __forceinline__ void finish_body(const Job &J, int wg, int nwg, const Gate &G,
+                                            const int32_t *partner = nullptr)
 {
     __shared__ int32_t sWave[GATE_THREADS / 64];
     __shared__ long long sBase;
@@ -948,12 +966,13 @@ __device__ __forceinline__ void finish_body(const Job &J, int wg, int nwg, const
     uint32_t C1 = 0u;
     int32_t slice = -1;
     bool acc = false;
+    const bool cross = SYM == SYM_NONE && G.cross_check;
     if (DEV_ANGLE) {
         // the column best is loaded first and decoded last: the device angles
         // are computed while it is in flight (its width is a template
         // argument, so the load is issued without a branch)
         unsigned long long raw = 0ull;
-        if (G.cross_check) {
+        if (cross) {
             const int j = cand ? I1 : 0;
             raw = NARROW ? (unsigned long long)reinterpret_cast<const uint32_t *>(J.cbest)[j]
                          : J.cbest[j];
@@ -975,11 +994,19 @@ __device__ __forceinline__ void finish_body(const Job &J, int wg, int nwg, const
     } else if (cand) {
         const double d1 = G.table[min(S1, (uint32_t)NORM2)];
         const double d2 = G.table[min(S2, (uint32_t)NORM2)];
-        if (G.cross_check)
+        if (cross)
             col_best_at(J, I1, C1, slice);
         acc = (d1 <= G.max_distance) && (d1 < G.max_ratio * d2);
     }
-    if (G.cross_check) {
+    if (SYM == SYM_COLUMNS) {
+        // every thread of the group leaves here: no barrier follows
+        if (i < J.nA)
+            J.rs1[i] = acc ? (uint32_t)I1 : 0xFFFFFFFFu;
+        return;
+    }
+    if (SYM == SYM_ROWS && acc)
+        acc = partner[I1] == i;
+    if (cross) {
         acc = acc && C1 == S1 && slice == i / SLICE;
         // Row i is its column's best only if no lower row of its 16-row
         // slice (the lanes below it in its 16-lane row) reaches C1 on that
@@ -1096,6 +1123,34 @@ __global__ __launch_bounds__(GATE_THREADS) void serac_finish_one(
     G.table = table;
     G.cross_check = cross_check;
     finish_body<true, NARROW>(J, blockIdx.x, (J.nA + GATE_THREADS - 1) / GATE_THREADS, G);
+}
+
+// The two passes of the symmetric column gates for one pair: SYM_COLUMNS on
+// the job of the swapped pair, then SYM_ROWS on the pair's own job with the
+// first pass's output as `partner`.
+template <int SYM>
+__global__ __launch_bounds__(GATE_THREADS) void serac_finish_sym(Job J, Gate G,
+                                                                 const int32_t *partner)
+{
+    finish_body<true, false, SYM>(J, blockIdx.x, (J.nA + GATE_THREADS - 1) / GATE_THREADS, G,
+                                  partner);
+}
+
+// The same for a batch: jobs [0, npairs) are the pairs, jobs [npairs,
+// 2 npairs) the swapped pairs in the same order.
+template <int SYM>
+__global__ __launch_bounds__(GATE_THREADS) void serac_finish_many_sym(
+    const Job *__restrict__ jobs, int gatePerJob, int npairs, Gate G)
+{
+    const int k = blockIdx.x / gatePerJob;
+    const Job J = jobs[SYM == SYM_COLUMNS ? npairs + k : k];
+    const int wg = blockIdx.x % gatePerJob;
+    const int nwg = (J.nA + GATE_THREADS - 1) / GATE_THREADS;
+    if (wg >= nwg)
+        return;
+    const int32_t *partner =
+        SYM == SYM_ROWS ? reinterpret_cast<const int32_t *>(jobs[npairs + k].rs1) : nullptr;
+    finish_body<false, false, SYM>(J, wg, nwg, G, partner);
 }
 
 __global__ __launch_bounds__(GATE_THREADS) void serac_finish_many(const Job *__restrict__ jobs,
@@ -1726,7 +1781,20 @@ bool bad_params(const serac_params *p)
         return true;
     if (p->cross_check != 0 && p->cross_check != 1)
         return true;
-    return p->flags != 0;
+    if (p->max_features < 0 || p->reserved != 0)
+        return true;
+    return (p->flags & ~SERAC_FLAG_SYMMETRIC) != 0;
+}
+
+// A set's descriptor count under the match cap.
+int32_t capped(int32_t n, const serac_params *p)
+{
+    return p->max_features > 0 ? std::min(n, p->max_features) : n;
+}
+
+bool symmetric(const serac_params *p)
+{
+    return (p->flags & SERAC_FLAG_SYMMETRIC) != 0;
 }
 
 bool misaligned(const void *p, uintptr_t align)
@@ -1859,17 +1927,26 @@ void launch_pair(Job &J, const Plan &p, const uint8_t *A, int nA, const uint8_t 
 // kernel after the finishing kernel clears what this call raised there, so
 // the region is zero whenever a call starts without the host tracking
 // anything, also when a captured graph of the call is replayed.
+// Clears the whole accumulator buffer of w if a failed call may have left it
+// raised (get_workspace does the same for the workspaces it hands out).
+int clear_if_dirty(Workspace *w, hipStream_t stream)
+{
+    if (!w->dirty)
+        return SERAC_OK;
+    serac_clear<<<1024, 256, 0, stream>>>(reinterpret_cast<uint4 *>(w->acc), w->acc_bytes / 16);
+    if (hipGetLastError() != hipSuccess)
+        return SERAC_ERR_HIP;
+    w->dirty = false;
+    w->acc_used[0] = w->acc_used[1] = 0;
+    return SERAC_OK;
+}
+
 int enqueue_pair(const Device *d, const Plan &p, Workspace *w, const uint8_t *A, int nA,
                  const uint8_t *B, int nB, const serac_params *params, const serac_matches *out,
                  hipStream_t stream, bool self_clear = false)
 {
-    if (w->dirty) {
-        serac_clear<<<1024, 256, 0, stream>>>(reinterpret_cast<uint4 *>(w->acc), w->acc_bytes / 16);
-        if (hipGetLastError() != hipSuccess)
-            return SERAC_ERR_HIP;
-        w->dirty = false;
-        w->acc_used[0] = w->acc_used[1] = 0;
-    }
+    if (clear_if_dirty(w, stream) != SERAC_OK)
+        return SERAC_ERR_HIP;
     Job J;
     const PrepJob none{};
     uint8_t *const region = self_clear ? w->acc : next_region(w);
@@ -1890,6 +1967,47 @@ int enqueue_pair(const Device *d, const Plan &p, Workspace *w, const uint8_t *A,
         serac_clear<<<(unsigned)std::min<size_t>((words + 255) / 256, 1024), 256, 0, stream>>>(
             reinterpret_cast<uint4 *>(region), words);
     }
+    if (hipGetLastError() != hipSuccess) {
+        mark_dirty(w);
+        return SERAC_ERR_HIP;
+    }
+    return SERAC_OK;
+}
+
+// Scratch of a pair under symmetric column gates: that of the pair (A, B)
+// with its prepared sets, then that of the swapped pair (B, A), whose rs1
+// holds the columns' accepted rows between the two finishing passes.
+size_t sym_aux_bytes(const Plan &pf, const Plan &pr, int nA, int nB)
+{
+    return align256(pf.scratch + pair_prep_bytes(nA, nB)) + pr.scratch + pair_prep_bytes(nB, nA);
+}
+
+// A pair under symmetric column gates (nA, nB > 0): the sweep of (B, A) and
+// its finishing pass, which writes each column's accepted row, then the
+// sweep of (A, B) and its finishing pass, which keeps row i where its best
+// column accepts i.  Neither sweep keeps column bests.  Each sweep takes an
+// accumulator region of its own in turn, like two calls.
+int enqueue_sym(const Device *d, const Plan &pf, const Plan &pr, Workspace *w, const uint8_t *A,
+                int nA, const uint8_t *B, int nB, const serac_params *params,
+                const serac_matches *out, hipStream_t stream)
+{
+    if (clear_if_dirty(w, stream) != SERAC_OK)
+        return SERAC_ERR_HIP;
+    const PrepJob none{};
+    uint8_t *const fa = w->aux;
+    uint8_t *const ra = w->aux + align256(pf.scratch + pair_prep_bytes(nA, nB));
+    Gate G = make_gate(d, params);
+    G.cross_check = 0;
+    Job Jr;
+    fill_job(Jr, pr, B, nB, none, A, nA, none, next_region(w), ra, nullptr, nullptr);
+    launch_pair(Jr, pr, B, nB, A, nA, ra + pr.scratch, take_clear(w, pr.acc), false, stream);
+    serac_finish_sym<SYM_COLUMNS>
+        <<<(nB + GATE_THREADS - 1) / GATE_THREADS, GATE_THREADS, 0, stream>>>(Jr, G, nullptr);
+    Job Jf;
+    fill_job(Jf, pf, A, nA, none, B, nB, none, next_region(w), fa, out->matches, out->count);
+    launch_pair(Jf, pf, A, nA, B, nB, fa + pf.scratch, take_clear(w, pf.acc), false, stream);
+    serac_finish_sym<SYM_ROWS><<<(nA + GATE_THREADS - 1) / GATE_THREADS, GATE_THREADS, 0, stream>>>(
+        Jf, G, reinterpret_cast<const int32_t *>(Jr.rs1));
     if (hipGetLastError() != hipSuccess) {
         mark_dirty(w);
         return SERAC_ERR_HIP;
@@ -1944,8 +2062,11 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int
                      const serac_params *params, const serac_matches *out)
 {
     return guarded([&]() -> int {
-        if (bad_set(descA, nA) || bad_set(descB, nB) || bad_params(params) || !out ||
-            bad_out(*out, nA))
+        if (bad_set(descA, nA) || bad_set(descB, nB) || bad_params(params) || !out)
+            return SERAC_ERR_INVALID_ARG;
+        nA = capped(nA, params);
+        nB = capped(nB, params);
+        if (bad_out(*out, nA))
             return SERAC_ERR_INVALID_ARG;
         if (out->capacity < nA)
             return SERAC_ERR_CAPACITY;
@@ -1961,6 +2082,14 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB, int
         const Plan p = make_plan(nA, nB, 0, d->cus);
         Workspace *w = nullptr;
         std::unique_lock<std::mutex> hold;
+        if (symmetric(params)) {
+            const Plan pr = make_plan(nB, nA, 0, d->cus);
+            st = get_workspace(stream, std::max(p.acc, pr.acc), sym_aux_bytes(p, pr, nA, nB), &w,
+                               hold);
+            if (st != SERAC_OK)
+                return st;
+            return enqueue_sym(d, p, pr, w, descA, nA, descB, nB, params, out, stream);
+        }
         st = get_workspace(stream, p.acc, p.scratch + pair_prep_bytes(nA, nB), &w, hold);
         if (st != SERAC_OK)
             return st;
@@ -1981,7 +2110,11 @@ int serac_match_pair_noalloc(const uint8_t *descA, int32_t nA, const uint8_t *de
 {
     return guarded([&]() -> int {
         if (bad_set(descA, nA) || bad_set(descB, nB) || bad_params(params) || !out ||
-            bad_out(*out, nA))
+            symmetric(params))
+            return SERAC_ERR_INVALID_ARG;
+        nA = capped(nA, params);
+        nB = capped(nB, params);
+        if (bad_out(*out, nA))
             return SERAC_ERR_INVALID_ARG;
         if (out->capacity < nA)
             return SERAC_ERR_CAPACITY;
@@ -2021,13 +2154,17 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
         for (int k = 0; k < num_images; ++k)
             if (bad_set(desc[k], n[k]))
                 return SERAC_ERR_INVALID_ARG;
+        // the counts under the match cap (the caller's n is not modified)
+        std::vector<int32_t> nc(num_images);
+        for (int k = 0; k < num_images; ++k)
+            nc[k] = capped(n[k], params);
         for (int q = 0; q < num_pairs; ++q) {
             const serac_pair pr = pairs[q];
             if (pr.a < 0 || pr.a >= num_images || pr.b < 0 || pr.b >= num_images)
                 return SERAC_ERR_INVALID_ARG;
-            if (bad_out(out[q], n[pr.a]))
+            if (bad_out(out[q], nc[pr.a]))
                 return SERAC_ERR_INVALID_ARG;
-            if (out[q].capacity < n[pr.a])
+            if (out[q].capacity < nc[pr.a])
                 return SERAC_ERR_CAPACITY;
         }
         Device *d = nullptr;
@@ -2035,18 +2172,21 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
         if (st != SERAC_OK)
             return st;
         hipStream_t stream = static_cast<hipStream_t>(params->stream);
+        const bool sym = symmetric(params);
 
         // pairs with an empty side only get a zero count
         std::vector<int32_t *> zero;
         std::vector<int> live;
         std::vector<char> asA(num_images, 0), asB(num_images, 0);
         for (int q = 0; q < num_pairs; ++q) {
-            if (n[pairs[q].a] == 0 || n[pairs[q].b] == 0) {
+            const serac_pair pr = pairs[q];
+            if (nc[pr.a] == 0 || nc[pr.b] == 0) {
                 zero.push_back(out[q].count);
             } else {
                 live.push_back(q);
-                asA[pairs[q].a] = 1;
-                asB[pairs[q].b] = 1;
+                asA[pr.a] = asB[pr.b] = 1;
+                if (sym)                          // and the swapped pair
+                    asA[pr.b] = asB[pr.a] = 1;
             }
         }
         // every image is prepared once, in the roles its pairs use
@@ -2055,24 +2195,33 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
         for (int k = 0; k < num_images; ++k) {
             if (asA[k] || asB[k]) {
                 prepped.push_back(k);
-                prep_total += prep_bytes(n[k], asA[k], asB[k]);
+                prep_total += prep_bytes(nc[k], asA[k], asB[k]);
             }
         }
-        // workgroups per pair: enough to fill the device a few times over
+        // Jobs: the live pairs, then (symmetric gates) the swapped pairs in
+        // the same order.  Workgroups per job: enough to fill the device a
+        // few times over.
         const int nlive = (int)live.size();
-        const long long target = nlive ? std::max(1LL, (4LL * d->cus + nlive - 1) / nlive) : 1;
-        std::vector<Plan> plans(nlive);
+        const int njobs = sym ? 2 * nlive : nlive;
+        auto job_sets = [&](int k, int &a, int &b) {
+            const serac_pair pr = pairs[live[k % std::max(nlive, 1)]];
+            a = k < nlive ? pr.a : pr.b;
+            b = k < nlive ? pr.b : pr.a;
+        };
+        const long long target = njobs ? std::max(1LL, (4LL * d->cus + njobs - 1) / njobs) : 1;
+        std::vector<Plan> plans(njobs);
         size_t acc_bytes = 0, res_bytes = 0;
         int unitsPerJob = 1, gatePerJob = 1;
-        for (int k = 0; k < nlive; ++k) {
-            const serac_pair pr = pairs[live[k]];
-            plans[k] = make_plan(n[pr.a], n[pr.b], target);
+        for (int k = 0; k < njobs; ++k) {
+            int a, b;
+            job_sets(k, a, b);
+            plans[k] = make_plan(nc[a], nc[b], target);
             acc_bytes += plans[k].acc;
             res_bytes += plans[k].scratch;
             unitsPerJob = std::max(unitsPerJob, plans[k].units());
-            gatePerJob = std::max(gatePerJob, (n[pr.a] + GATE_THREADS - 1) / GATE_THREADS);
+            gatePerJob = std::max(gatePerJob, (nc[a] + GATE_THREADS - 1) / GATE_THREADS);
         }
-        const size_t jobs_bytes = align256(sizeof(Job) * (size_t)std::max(nlive, 1));
+        const size_t jobs_bytes = align256(sizeof(Job) * (size_t)std::max(njobs, 1));
         const size_t prepjobs_bytes = align256(sizeof(PrepJob) * std::max<size_t>(prepped.size(), 1));
         const size_t zero_bytes = align256(sizeof(int32_t *) * zero.size() + 8);
         const size_t host_bytes = jobs_bytes + prepjobs_bytes + zero_bytes;
@@ -2095,21 +2244,24 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
         int prepBlocks = 1;
         for (size_t k = 0; k < prepped.size(); ++k) {
             const int im = prepped[k];
-            pjobs[k] = make_prep(desc[im], n[im], asA[im], asB[im], pq);
+            pjobs[k] = make_prep(desc[im], nc[im], asA[im], asB[im], pq);
             slot[im] = (int)k;
             prepBlocks = std::max(prepBlocks, prep_blocks(pjobs[k]));
         }
         uint8_t *q = next_region(w);
         bool narrow = true;                      // 32-bit column bests for every pair of the batch
-        for (int k = 0; k < nlive; ++k) {
-            const serac_pair pr = pairs[live[k]];
-            fill_job(jobs[k], plans[k], desc[pr.a], n[pr.a], pjobs[slot[pr.a]], desc[pr.b], n[pr.b],
-                     pjobs[slot[pr.b]], q, rq, out[live[k]].matches, out[live[k]].count);
+        for (int k = 0; k < njobs; ++k) {
+            int a, b;
+            job_sets(k, a, b);
+            const bool own = k < nlive;
+            fill_job(jobs[k], plans[k], desc[a], nc[a], pjobs[slot[a]], desc[b], nc[b],
+                     pjobs[slot[b]], q, rq, own ? out[live[k]].matches : nullptr,
+                     own ? out[live[k]].count : nullptr);
             narrow = narrow && jobs[k].cb32;
             q += plans[k].acc;
             rq += plans[k].scratch;
         }
-        for (int k = 0; k < nlive; ++k)          // one sweep kernel: one format for all pairs
+        for (int k = 0; k < njobs; ++k)          // one sweep kernel: one format for all pairs
             jobs[k].cb32 = narrow ? 1 : 0;
         for (size_t k = 0; k < zero.size(); ++k)
             zp[k] = zero[k];
@@ -2128,14 +2280,15 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
             C.stride = (uint32_t)prepBlocks * PREP_THREADS;
             serac_prep_many<<<dim3(prepBlocks, (unsigned)prepped.size()), PREP_THREADS, 0, stream>>>(
                 dpjobs, C);
-            const Gate G = make_gate(d, params);
+            Gate G = make_gate(d, params);
+            const bool cols = params->cross_check && !sym;
             hipEvent_t e0, e1;
             prof_slot(e0, e1,
-                      !params->cross_check ? "serac_tiles_many<false, false>"
-                      : narrow             ? "serac_tiles_many<true, true>"
-                                           : "serac_tiles_many<true, false>");
-            const dim3 grid(nlive * unitsPerJob);
-            if (!params->cross_check)
+                      !cols    ? "serac_tiles_many<false, false>"
+                      : narrow ? "serac_tiles_many<true, true>"
+                               : "serac_tiles_many<true, false>");
+            const dim3 grid(njobs * unitsPerJob);
+            if (!cols)
                 hipExtLaunchKernelGGL(serac_tiles_many<false, false>, grid, dim3(TILE_THREADS), 0,
                                       stream, e0, e1, 0, djobs, unitsPerJob);
             else if (narrow)
@@ -2144,8 +2297,16 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
             else
                 hipExtLaunchKernelGGL(serac_tiles_many<true, false>, grid, dim3(TILE_THREADS), 0,
                                       stream, e0, e1, 0, djobs, unitsPerJob);
-            serac_finish_many<<<nlive * gatePerJob, GATE_THREADS, 0, stream>>>(djobs, gatePerJob,
-                                                                              G);
+            if (sym) {
+                G.cross_check = 0;
+                serac_finish_many_sym<SYM_COLUMNS><<<nlive * gatePerJob, GATE_THREADS, 0, stream>>>(
+                    djobs, gatePerJob, nlive, G);
+                serac_finish_many_sym<SYM_ROWS><<<nlive * gatePerJob, GATE_THREADS, 0, stream>>>(
+                    djobs, gatePerJob, nlive, G);
+            } else {
+                serac_finish_many<<<nlive * gatePerJob, GATE_THREADS, 0, stream>>>(djobs,
+                                                                                  gatePerJob, G);
+            }
         }
         if (e == hipSuccess)
             e = hipGetLastError();

@@ -10,7 +10,7 @@ too, so a test can tell a changed generator from a changed matcher.
 SHA-256 identity of the correspondence blobs is the referee the SERAC README
 uses for its two arms (section "Exactness").
 
-Run from the repository root (about 8 minutes on 8 cores, most of it the
+Run from the repository root (about 40 minutes on 8 cores, most of it the
 1128 pairs of the exhaustive 48 x 8192 batch):
 
     python3 tests/golden/make_oracle_hashes.py

@@ -52,10 +52,11 @@ def test_status_strings():
 
 
 def _p(**kw):
-    d = dict(max_ratio=0.8, max_distance=math.inf, cross_check=1, flags=0, stream=None)
+    d = dict(max_ratio=0.8, max_distance=math.inf, cross_check=1, flags=0, stream=None,
+             max_features=0, reserved=0)
     d.update(kw)
     return serac_params(d["max_ratio"], d["max_distance"], d["cross_check"], d["flags"],
-                        d["stream"])
+                        d["stream"], d["max_features"], d["reserved"])
 
 
 def _m(cap=100):
@@ -72,7 +73,8 @@ def call_pair(a=FAKE, nA=10, b=FAKE, nB=10, params="ok", out="ok"):
 BAD_PARAMS = [
     dict(max_ratio=float("nan")), dict(max_ratio=0.0), dict(max_ratio=-1.0),
     dict(max_ratio=math.inf), dict(max_distance=float("nan")),
-    dict(max_distance=-0.1), dict(cross_check=2), dict(cross_check=-1), dict(flags=1),
+    dict(max_distance=-0.1), dict(cross_check=2), dict(cross_check=-1), dict(flags=2),
+    dict(flags=-1), dict(flags=3), dict(max_features=-1), dict(reserved=1),
 ]
 
 
@@ -122,6 +124,8 @@ def test_match_pair_noalloc_validation():
     assert call(nA=-1) == E
     assert call(params=_p(flags=1)) == E
     assert call(params=_p(max_ratio=0.0)) == E
+    assert call(params=_p(flags=serac.SERAC_FLAG_SYMMETRIC)) == E     # not on this path
+    assert call(params=_p(max_features=-3)) == E
     assert call(out=serac_matches(FAKE + 4, 100, FAKE)) == E
     assert L.serac_match_pair_noalloc(FAKE, 10, FAKE, 10, None, ctypes.byref(_m())) == E
     assert L.serac_match_pair_noalloc(FAKE, 10, FAKE, 10, ctypes.byref(_p()), None) == E
@@ -135,6 +139,19 @@ def test_match_pair_noalloc_validation():
 def test_match_pair_rejects_small_capacity():
     assert call_pair(nA=101) == serac.SERAC_ERR_CAPACITY
     assert call_pair(nA=10, out=ctypes.byref(_m(9))) == serac.SERAC_ERR_CAPACITY
+    # under a match cap the capacity needed is min(nA, max_features)
+    capped = ctypes.byref(_p(max_features=150))
+    assert call_pair(nA=200, params=capped) == serac.SERAC_ERR_CAPACITY
+    assert call_pair(nA=200, params=capped, out=ctypes.byref(_m(149))) == \
+        serac.SERAC_ERR_CAPACITY
+
+
+def test_params_layout():
+    """The binding's structure has the header's layout (x86-64)."""
+    assert ctypes.sizeof(serac_params) == 40
+    assert serac_params.stream.offset == 24
+    assert serac_params.max_features.offset == 32
+    assert serac_params.reserved.offset == 36
 
 
 def test_match_pairs_validation():
