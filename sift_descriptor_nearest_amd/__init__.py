@@ -16,7 +16,9 @@ __all__ = ["match_pair", "match_pair_into", "match_pairs", "match_pairs_host", "
            "profile_start", "profile_stop", "SeracError", "library", "LIB_PATH"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libserac.so")
+# SERAC_LIBRARY_PATH selects another build of the same library (the
+# sanitizer tests load a host-sanitized build this way)
+LIB_PATH = os.environ.get("SERAC_LIBRARY_PATH") or os.path.join(HERE, "libserac.so")
 MAX_DESCRIPTORS = 262144
 
 SERAC_OK = 0
