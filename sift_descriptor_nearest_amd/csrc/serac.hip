@@ -78,6 +78,8 @@
 #include <algorithm>
 #include <deque>
 #include <mutex>
+#include <numeric>
+#include <atomic>
 #include <new>
 #include <type_traits>
 #include <vector>
@@ -420,6 +422,23 @@ __global__ __launch_bounds__(PREP_THREADS) void serac_prep_many(const PrepJob *_
 // terms in the prologue, and each chunk of B in two stages, a copy of the
 // raw chunk into LDS and, during the chunk before the one that needs it,
 // its conversion into the operand planes and the columns' key addends.
+// Workgroup order: the tile a workgroup sweeps is (a * x + b) mod n of its
+// dispatch index x, a bijection for gcd(a, n) = 1 (the host keeps
+// a * (n - 1) + b below 2^32).  The library launches
+// with a = 1, b = 0 (the XCD-aware map below); other values only come from a
+// test hook that checks that results do not depend on the order in which
+// workgroups run (their merges are all order-independent maxima).
+struct WgOrder {
+    uint32_t a, b;
+};
+
+__device__ __forceinline__ int wg_index(uint32_t x, WgOrder o, uint32_t n)
+{
+    if (o.a == 1u && o.b == 0u)
+        return (int)x;
+    return (int)((o.a * x + o.b) % n);
+}
+
 template <bool COLS, bool FUSED, bool NARROW>
 __device__ __forceinline__ void tiles_body(const Job &J, int u)
 {
@@ -791,9 +810,9 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
 
 // NARROW: the column bests take 32 bits (J.cb32; see col_best_at).
 template <bool COLS, bool NARROW>
-__global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_one(Job J)
+__global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_one(Job J, WgOrder o)
 {
-    tiles_body<COLS, false, NARROW>(J, blockIdx.x);
+    tiles_body<COLS, false, NARROW>(J, wg_index(blockIdx.x, o, (uint32_t)(J.nRB * J.Gc)));
 }
 
 // One pair straight from the raw descriptors (no preparation kernel); also
@@ -808,7 +827,8 @@ __global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_one(Job J)
 template <bool COLS, bool NARROW>
 __global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_fused(
     const uint8_t *A, const uint8_t *B, int32_t nA, int32_t nB, int32_t nRB, int32_t nBC,
-    int32_t gch, uint4 *clear_p, uint32_t clear_words, uint32_t clear_stride, Job J)
+    int32_t gch, uint4 *clear_p, uint32_t clear_words, uint32_t clear_stride, uint32_t order_a,
+    uint32_t order_b, uint32_t units, Job J)
 {
     J.A = A;
     J.B = B;
@@ -818,15 +838,17 @@ __global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_fused(
     J.nBC = nBC;
     J.gch = gch;
     clear_body<TILE_THREADS>(Clear{clear_p, clear_words, clear_stride});
-    tiles_body<COLS, true, NARROW>(J, blockIdx.x);
+    tiles_body<COLS, true, NARROW>(J, wg_index(blockIdx.x, WgOrder{order_a, order_b}, units));
 }
 
 template <bool COLS, bool NARROW>
 __global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_many(const Job *__restrict__ jobs,
-                                                                    int unitsPerJob)
+                                                                    int unitsPerJob, WgOrder o,
+                                                                    uint32_t blocks)
 {
-    const Job J = jobs[blockIdx.x / unitsPerJob];
-    const int u = blockIdx.x % unitsPerJob;
+    const int x = wg_index(blockIdx.x, o, blocks);
+    const Job J = jobs[x / unitsPerJob];
+    const int u = x % unitsPerJob;
     if (u >= J.nRB * J.Gc)
         return;
     tiles_body<COLS, false, NARROW>(J, u);
@@ -1350,6 +1372,27 @@ double angle_slack(const double *table)
 
 int fixed_setup(int dev);
 
+// Test hook SERAC_TEST_WG_ORDER=<seed> (read at a device's set-up; 0 or
+// unset: the library's own order): the tile kernels sweep their tiles in a
+// permuted workgroup order (see WgOrder).
+std::atomic<uint32_t> g_order_seed{0};
+
+WgOrder wg_order(uint32_t n)
+{
+    const uint32_t seed = g_order_seed.load(std::memory_order_relaxed);
+    if (seed == 0u || n <= 1u)
+        return WgOrder{1u, 0u};
+    const uint32_t b = (uint32_t)((seed * 40503ull) % n);
+    uint32_t a = (uint32_t)((seed * 2654435761ull) % n) | 1u;
+    while (std::gcd(a % n, n) != 1u)
+        a += 2u;
+    a %= n;
+    // (a * x + b) must not wrap in 32 bits; a rotation always fits
+    if ((unsigned long long)a * (n - 1) + b >= (1ull << 32))
+        a = 1u;
+    return WgOrder{a, b};
+}
+
 // Per-device set-up: architecture check, acos table and the device angle's
 // distance from it, the fixed scratch of the non-allocating entry point,
 // pool threshold.
@@ -1381,6 +1424,12 @@ int device_setup(Device **out)
             const long v = std::strtol(e, &end, 10);
             if (end != e && v >= -1 && v <= (1L << 30))
                 d.spin_limit = (int)v;
+        }
+        if (const char *e = std::getenv("SERAC_TEST_WG_ORDER")) {
+            char *end = nullptr;
+            const unsigned long v = std::strtoul(e, &end, 10);
+            if (end != e && v <= 0xFFFFFFFFul)
+                g_order_seed.store((uint32_t)v, std::memory_order_relaxed);
         }
         // angle of every attainable clamped score, with the C library's acos
         std::vector<double> t(NORM2 + 1);
@@ -1834,11 +1883,12 @@ void launch_one(const Job &J, int units, hipStream_t stream)
 {
     hipEvent_t e0, e1;
     prof_slot(e0, e1, tile_name<COLS, NARROW>(false));
+    const WgOrder o = wg_order((uint32_t)units);
     if (e0)
         hipExtLaunchKernelGGL(serac_tiles_one<COLS, NARROW>, dim3(units), dim3(TILE_THREADS), 0,
-                              stream, e0, e1, 0, J);
+                              stream, e0, e1, 0, J, o);
     else
-        serac_tiles_one<COLS, NARROW><<<units, TILE_THREADS, 0, stream>>>(J);
+        serac_tiles_one<COLS, NARROW><<<units, TILE_THREADS, 0, stream>>>(J, o);
 }
 
 void launch_tiles(const Job &J, const Plan &p, bool cols, hipStream_t stream)
@@ -1876,13 +1926,15 @@ void launch_fused(const Job &J, uint4 *clear_p, uint32_t clear_words, uint32_t c
 {
     hipEvent_t e0, e1;
     prof_slot(e0, e1, tile_name<COLS, NARROW>(true));
+    const WgOrder o = wg_order((uint32_t)units);
     if (e0)
         hipExtLaunchKernelGGL(serac_tiles_fused<COLS, NARROW>, dim3(units), dim3(TILE_THREADS), 0,
                               stream, e0, e1, 0, J.A, J.B, J.nA, J.nB, J.nRB, J.nBC, J.gch,
-                              clear_p, clear_words, clear_stride, J);
+                              clear_p, clear_words, clear_stride, o.a, o.b, (uint32_t)units, J);
     else
         serac_tiles_fused<COLS, NARROW><<<units, TILE_THREADS, 0, stream>>>(
-            J.A, J.B, J.nA, J.nB, J.nRB, J.nBC, J.gch, clear_p, clear_words, clear_stride, J);
+            J.A, J.B, J.nA, J.nB, J.nRB, J.nBC, J.gch, clear_p, clear_words, clear_stride, o.a,
+            o.b, (uint32_t)units, J);
 }
 
 // Preparation and tile sweep of one pair (nA, nB > 0) on `stream`; the
@@ -2288,15 +2340,16 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
                       : narrow ? "serac_tiles_many<true, true>"
                                : "serac_tiles_many<true, false>");
             const dim3 grid(njobs * unitsPerJob);
+            const WgOrder o = wg_order(grid.x);
             if (!cols)
                 hipExtLaunchKernelGGL(serac_tiles_many<false, false>, grid, dim3(TILE_THREADS), 0,
-                                      stream, e0, e1, 0, djobs, unitsPerJob);
+                                      stream, e0, e1, 0, djobs, unitsPerJob, o, grid.x);
             else if (narrow)
                 hipExtLaunchKernelGGL(serac_tiles_many<true, true>, grid, dim3(TILE_THREADS), 0,
-                                      stream, e0, e1, 0, djobs, unitsPerJob);
+                                      stream, e0, e1, 0, djobs, unitsPerJob, o, grid.x);
             else
                 hipExtLaunchKernelGGL(serac_tiles_many<true, false>, grid, dim3(TILE_THREADS), 0,
-                                      stream, e0, e1, 0, djobs, unitsPerJob);
+                                      stream, e0, e1, 0, djobs, unitsPerJob, o, grid.x);
             if (sym) {
                 G.cross_check = 0;
                 serac_finish_many_sym<SYM_COLUMNS><<<nlive * gatePerJob, GATE_THREADS, 0, stream>>>(
