@@ -43,6 +43,14 @@ tests/golden/oracle_hashes.json.
 `--mfma-ceiling` measures the int8 MFMA ceiling of the device, the shader
 clock it runs at, and what vector instructions issued beside MFMAs cost
 (libserac_probe.so), the figures the sweep's bound is derived from.
+
+`--f1-probe` bounds what reusing staged A tiles across the pairs of a batch
+could save: the fixed per-workgroup part of batch sweeps of 1 to 32 chunks.
+
+`--copy-probe MIB` and `--write-traffic DIR` make the traffic record: the
+first runs a plain copy of known size for the counter scales, the second
+(on any host) turns four rocprofv3 FETCH_SIZE / WRITE_SIZE runs into
+profiles/traffic_tiles_pair_8192x8192.json.
 """
 from __future__ import annotations
 
@@ -94,7 +102,76 @@ def measured_traffic():
         return None, "kernel changed since the committed counter run"
     return t.get("bytes_per_launch"), (
         f"committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs ({os.path.relpath(TRAFFIC, ROOT)}, "
-        f"kernel sha256 {t['kernel_sha256'][:16]}..., command: {t.get('command', '?')})")
+        f"kernel sha256 {t['kernel_sha256'][:16]}..., commands in that file)")
+
+
+TRAFFIC_RUNS = ("fetch", "write", "copy_fetch", "copy_write")
+COPY_PROBE_MIB = 256
+
+
+def counter_rows(folder: str):
+    """(kernel name, counter name, value) of every dispatch in the
+    rocprofv3 --pmc CSV output under `folder`."""
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(folder, "**", "*counter_collection.csv"),
+                                 recursive=True)):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no rocprofv3 counter CSV under {folder}")
+    return rows
+
+
+def write_traffic(folder: str, kernel: str, workload: str) -> int:
+    """Writes the traffic record from four rocprofv3 --pmc runs kept under
+    folder/{fetch,write,copy_fetch,copy_write}: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch) of `kernel` in this benchmark, and of the copy
+    probe, whose bytes are known and give each counter's scale."""
+    def per_dispatch(run, counter, match, largest=None):
+        v = [x for k, c, x in counter_rows(os.path.join(folder, run))
+             if c == counter and match in k]
+        if largest:
+            v = sorted(v)[-largest:]
+        if not v:
+            raise SystemExit(f"{run}: no {counter} of a kernel named like {match!r}")
+        return sum(v) / len(v), len(v)
+
+    fetch, nf = per_dispatch("fetch", "FETCH_SIZE", kernel)
+    write, nw = per_dispatch("write", "WRITE_SIZE", kernel)
+    copy_bytes = COPY_PROBE_MIB << 20
+    cf, _ = per_dispatch("copy_fetch", "FETCH_SIZE", "copyBuffer", largest=10)
+    cw, _ = per_dispatch("copy_write", "WRITE_SIZE", "copyBuffer", largest=10)
+    fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    bench = "python3 <repo>/bench.py --gpus 1 --steps 20 --warmup 5 --no-cpu-baseline"
+    probe = f"python3 <repo>/bench.py --copy-probe {COPY_PROBE_MIB}"
+    rec = {
+        "kernel": kernel, "workload": workload, "kernel_sha256": kernel_sha(),
+        "fetch_size_kib_per_launch": round(fetch, 1), "write_size_kib_per_launch": round(write, 1),
+        "dispatches": [nf, nw],
+        "copy_probe_bytes": copy_bytes, "copy_probe_fetch_size_kib": round(cf, 4),
+        "copy_probe_write_size_kib": round(cw, 4),
+        "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+        "bytes_per_launch": int(round(fetch * 1024 * fs + write * 1024 * ws)),
+        "commands": [
+            "cd /tmp && export TMPDIR=/tmp",
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/fetch -o run -- {bench}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/write -o run -- {bench}",
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/copy_fetch -o run -- {probe}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/copy_write -o run -- {probe}",
+            f"python3 <repo>/bench.py --write-traffic <out>",
+        ],
+        "note": "per-dispatch means over the tile kernel's dispatches in each bench run; "
+                "the copy probe is 10 copies of a 256 MiB buffer (the runtime's copy kernel), "
+                "its counters against the bytes it moves give the scales",
+    }
+    with open(TRAFFIC, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec), flush=True)
+    return 0
 
 
 def cpu_model() -> str:
@@ -167,11 +244,21 @@ def main() -> int:
                     help="instead of the benchmark, measure the int8 MFMA ceiling, the "
                          "shader clock and the issue cost of vector instructions beside "
                          "MFMAs (one JSON line)")
+    ap.add_argument("--f1-probe", action="store_true",
+                    help="instead of the benchmark, bound what cross-pair reuse of A tiles in "
+                         "a batch could save (one JSON line)")
+    ap.add_argument("--write-traffic", metavar="DIR",
+                    help="on any host: write the traffic record from the four rocprofv3 "
+                         "--pmc runs under DIR/{fetch,write,copy_fetch,copy_write}")
+    ap.add_argument("--traffic-kernel", default="serac_tiles_fused<true, true>",
+                    help="the kernel --write-traffic reads (the bench line's roofline kernel)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, copy a MIB-MiB device buffer 10 times "
                          "(a plain copy kernel of known traffic, for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.write_traffic:
+        return write_traffic(args.write_traffic, args.traffic_kernel, args.workload)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, "
@@ -206,6 +293,8 @@ def main() -> int:
         return host_pipeline(serac, synth, torch, np)
     if args.configs:
         return all_configs(serac, synth, torch, np)
+    if args.f1_probe:
+        return f1_probe(serac, synth, torch, np)
     dev = torch.device("cuda:0")
     p = synth.workload(args.workload)
     nA, nB = p.A.shape[0], p.B.shape[0]
@@ -465,6 +554,59 @@ def host_pipeline(serac, synth, torch, np, reps: int = 5) -> int:
         "unpipelined_ms_per_pair": round(stages[P], 5),
         "device_only_ms_per_pair": round(dev_ms, 5),
         "matches": int(sum(len(x) for x in ref)),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def f1_probe(serac, synth, torch, np, reps: int = 7) -> int:
+    """What cross-pair reuse of A tiles in a batch could save at most.
+
+    A batch workgroup sweeps one 256-row block of A against one pair's B
+    (all of it: the exhaustive batch's pairs have one column group).  Its
+    time is a fixed part (loading its rows of A, the lane merge, the slot
+    and column-best writes) plus one part per 256-column chunk of B.  Reuse
+    of the A tile across several B images could remove at most the fixed
+    part of every sweep after the first.  Batches of 64 pairs (8 images of
+    8192 rows against 8 of nB rows: 2048 workgroups, 8 rounds of 256) with
+    nB = 256 c for c = 1 ... 32 chunks give the tile kernel's time per
+    round; a least-squares line through them splits it into the fixed part
+    and the per-chunk part."""
+    warm_device(serac, synth, torch)
+    rng = np.random.default_rng(11)
+    A = [torch.from_numpy(synth.desc(rng, 8192)).to("cuda:0") for _ in range(8)]
+    rows = {}
+    rounds = None
+    for c in (1, 2, 4, 8, 16, 32):
+        B = [torch.from_numpy(synth.desc(rng, 256 * c)).to("cuda:0") for _ in range(8)]
+        imgs = A + B
+        pairs = [(a, 8 + b) for a in range(8) for b in range(8)]
+        serac.match_pairs(imgs, pairs)            # warm-up: workspace, staging
+        torch.cuda.synchronize()
+        per = []
+        for _ in range(reps):
+            serac.profile_start(1, 1)
+            serac.match_pairs(imgs, pairs)
+            torch.cuda.synchronize()
+            _, n, ms, name = serac.profile_stop()
+            per.append(ms[0] * 1e3)
+        units = 64 * 32                            # pairs x row blocks, one column group each
+        rounds = -(-units // 256)
+        rows[c] = {"kernel": name, "kernel_us_median": round(float(np.median(per)), 3),
+                   "us_per_round": round(float(np.median(per)) / rounds, 4)}
+    cs = np.array(sorted(rows), dtype=float)
+    ts = np.array([rows[int(c)]["us_per_round"] for c in cs])
+    slope, fixed = np.polyfit(cs, ts, 1)
+    line = {
+        "metric": "upper bound on cross-pair A-tile reuse gain, exhaustive batch of 8192-row images",
+        "value": round(float(fixed / (fixed + 32 * slope)), 4), "unit": "fraction of tile time",
+        "higher_is_better": False, "n_gpus": 1, "reps": reps,
+        "fixed_us_per_workgroup": round(float(fixed), 4),
+        "chunk_us_per_workgroup": round(float(slope), 4),
+        "rounds_per_launch": rounds,
+        "per_chunk_count": {str(k): v for k, v in rows.items()},
+        "note": "fixed = A-tile load + lane merge + slot/column writes per workgroup; reuse "
+                "could save at most the A-tile part of it",
     }
     print(json.dumps(line), flush=True)
     return 0
