@@ -331,6 +331,15 @@ __device__ __forceinline__ void load_lds16(const void *src, void *lds_wave_base)
     asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
 }
 
+// The same from a wave-uniform base (in SGPRs) plus a 32-bit per-lane byte
+// offset: no per-lane address arithmetic when only the base moves.
+__device__ __forceinline__ void load_lds16(const void *sbase, uint32_t voff, void *lds_wave_base)
+{
+    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void_ptr)lds_wave_base;
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0)
+                 : "memory");
+}
+
 // ------------------------------------------------------------ preparation
 
 // Converts one set: one thread per (row, 16-byte part), eight threads per
@@ -466,13 +475,24 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     const int hf = lane & 1;
     const int hcol = 64 * (lane >> 4) + 8 * w + ((lane >> 1) & 7);
     auto fetch_raw = [&](int c) {
+        const int col0 = (c0 + c) * CHUNK;
+        if (col0 + CHUNK <= J.nB) {
+            // a whole chunk: 32 KiB from one scalar base, the lane offsets fixed
+            const uint8_t *base = J.B + (size_t)col0 * DIM;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int off = k * (TILE_THREADS * 16) + tid * 16;    // byte of the chunk
-            const int col = (c0 + c) * CHUNK + off / DIM;
-            const uint8_t *src = col < J.nB ? J.B + (size_t)col * DIM + off % DIM
-                                            : g_zero_desc + off % DIM;
-            load_lds16(src, sRaw + k * (TILE_THREADS * 16) + w * 1024);
+            for (int k = 0; k < 4; ++k)
+                load_lds16(base + k * (TILE_THREADS * 16), (uint32_t)tid * 16u,
+                           sRaw + k * (TILE_THREADS * 16) + w * 1024);
+        } else {
+            // the ragged last chunk: columns past the set read the zero descriptor
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int off = k * (TILE_THREADS * 16) + tid * 16;    // byte of the chunk
+                const int col = col0 + off / DIM;
+                const uint8_t *src = col < J.nB ? J.B + (size_t)col * DIM + off % DIM
+                                                : g_zero_desc + off % DIM;
+                load_lds16(src, sRaw + k * (TILE_THREADS * 16) + w * 1024);
+            }
         }
     };
     auto convert = [&](int c, int buf) {
