@@ -312,6 +312,16 @@ __device__ __forceinline__ void lds_barrier()
 
 typedef __attribute__((address_space(3))) void *lds_void_ptr;
 
+// 16 bytes through a global-address-space pointer: a generic pointer that
+// may point at a __device__ array (the zero descriptor) would otherwise be
+// read with a flat load, which also waits on and counts as an LDS access.
+__device__ __forceinline__ uint4 load_global16(const void *p)
+{
+    typedef uint32_t gv4 __attribute__((ext_vector_type(4)));
+    const gv4 x = *(const __attribute__((address_space(1))) gv4 *)p;
+    return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
 // 16 bytes per lane from global memory straight into LDS: lane l of the
 // wave writes bytes [16*l, 16*l + 16) after `lds_wave_base`, which must be
 // the same for the whole wave.
@@ -332,12 +342,16 @@ __device__ __forceinline__ void load_lds16(const void *src, void *lds_wave_base)
 }
 
 // The same from a wave-uniform base (in SGPRs) plus a 32-bit per-lane byte
-// offset: no per-lane address arithmetic when only the base moves.
+// offset: no per-lane address arithmetic when only the base moves.  The
+// base goes through readfirstlane, so that it is in SGPRs even where the
+// compiler cannot prove it uniform (where it can, that costs nothing).
 __device__ __forceinline__ void load_lds16(const void *sbase, uint32_t voff, void *lds_wave_base)
 {
     const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void_ptr)lds_wave_base;
-    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0)
-                 : "memory");
+    const uint64_t b = (uint64_t)(uintptr_t)sbase;
+    const uint64_t u = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b) |
+                       ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32);
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(u), "{m0}"(m0) : "memory");
 }
 
 // ------------------------------------------------------------ preparation
@@ -529,7 +543,7 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
         uint4 v4[4];
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc)
-            v4[kc] = *reinterpret_cast<const uint4 *>(ra + 32 * kc);
+            v4[kc] = load_global16(ra + 32 * kc);
         uint32_t sa = 0u;
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
@@ -775,9 +789,11 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
 
     // ---- merge the 32 lanes that share each row, through this wave's own
     // LDS scratch (no barrier: only this wave writes and reads it): lane pair
-    // (q, q + 32) folds the entries of source lanes 0..15 and 16..31 of row
-    // q in ascending order, so on a key tie (same score, same tile) the
-    // first, lowest lane, which is the lowest column, stays.
+    // (q, q + 32) merges the entries of source lanes 0..15 and 16..31 of row
+    // q pairwise in a four-level tree (dependency depth 4 instead of a
+    // 16-step chain), the lower source lane first in every pair, so on a
+    // key tie (same score, same tile) the lowest lane, which is the lowest
+    // column, stays.
     // Entry e of row r sits at 33*r + e (rows padded by one entry): the
     // stores of one row and the loads of one entry from 32 rows both fall on
     // distinct banks, and every access is a fixed offset from a per-lane
@@ -797,16 +813,27 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     for (int rr = 0; rr < 16; ++rr)
         wb[SCR_ROW * rr] = make_uint2(b1[rr], b2[rr]);
     const uint2 *const rbp = scr + SCR_ROW * n + 16 * h;
-    uint32_t K1 = 0u, K2 = 0u;
-    int k1 = 0;                                          // K1 came from source lane 16h + k1
+    uint32_t t1[16], t2[16];
+    int tl[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-        const uint2 e = rbp[k];                          // row n, entry 16h + k
-        k1 = e.x > K1 ? k : k1;
-        K2 = umax3(min(K1, e.x), K2, e.y);
-        K1 = max(K1, e.x);
+        const uint2 e = rbp[k];
+        t1[k] = e.x;
+        t2[k] = e.y;
+        tl[k] = k;
     }
-    int L1 = 16 * h + k1;                                // source lane (column in the tile)
+#pragma unroll
+    for (int s = 1; s < 16; s *= 2) {
+#pragma unroll
+        for (int k = 0; k < 16; k += 2 * s) {
+            const uint32_t a1 = t1[k], b1 = t1[k + s];
+            tl[k] = b1 > a1 ? tl[k + s] : tl[k];
+            t2[k] = umax3(min(a1, b1), t2[k], t2[k + s]);
+            t1[k] = max(a1, b1);
+        }
+    }
+    uint32_t K1 = t1[0], K2 = t2[0];
+    int L1 = 16 * h + tl[0];                             // source lane (column in the tile)
     {
         // lane half 0 holds the lower source lanes: it keeps its own on a tie
         const uint32_t o1 = __shfl_xor(K1, 32), o2 = __shfl_xor(K2, 32);

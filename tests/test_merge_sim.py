@@ -4,7 +4,7 @@ The tile kernel never holds a row's scores together: each of the 32 lanes
 that share a row sees one column per 32-column tile, keeps a running best
 and runner-up of packed keys (S << 9 | 511 - t) over tile pairs with
 max3 / med3 (the second-best update deferred to every other pair), the
-lanes are merged in ascending order, and the column groups of a row meet
+lanes are merged pairwise in a tree (lower lane first in every pair), and the column groups of a row meet
 only as packed 64-bit slots in the finishing kernel.  The column side
 raises (S << 9 | 511 - slice) by atomic maxima and settles the lowest row
 of a 16-row slice with bounds from the rows' own top-2.  The result must not
@@ -66,18 +66,24 @@ def lane_sweep(S, c0, ncols):
         else:
             tk = md
     assert npairs % 2 == 0                            # a chunk is four pairs
-    # lane merge: halves 0..15 and 16..31 in ascending order, then across
+    # lane merge: within each half (source lanes 0..15, 16..31) a pairwise
+    # tree, the lower lane first in every pair; then across the halves
     K1 = np.zeros((T, 2), np.uint64)
     K2 = np.zeros((T, 2), np.uint64)
     L = np.zeros((T, 2), np.int64)
     for h in range(2):
-        k1 = np.zeros(T, np.int64)
-        for k in range(16):
-            ex, ey = b1[:, 16 * h + k], b2[:, 16 * h + k]
-            k1 = np.where(ex > K1[:, h], k, k1)
-            K2[:, h] = np.maximum(np.maximum(np.minimum(K1[:, h], ex), K2[:, h]), ey)
-            K1[:, h] = np.maximum(K1[:, h], ex)
-        L[:, h] = 16 * h + k1
+        t1 = [b1[:, 16 * h + k] for k in range(16)]
+        t2 = [b2[:, 16 * h + k] for k in range(16)]
+        tl = [np.full(T, k, np.int64) for k in range(16)]
+        s = 1
+        while s < 16:
+            for k in range(0, 16, 2 * s):
+                a1, c1 = t1[k], t1[k + s]
+                tl[k] = np.where(c1 > a1, tl[k + s], tl[k])
+                t2[k] = np.maximum(np.maximum(np.minimum(a1, c1), t2[k]), t2[k + s])
+                t1[k] = np.maximum(a1, c1)
+            s *= 2
+        K1[:, h], K2[:, h], L[:, h] = t1[0], t2[0], 16 * h + tl[0]
     # half 0 keeps its own on a key tie (it holds the lower lanes)
     o1, o2, oL = K1[:, 1], K2[:, 1], L[:, 1]
     A1, A2, AL = K1[:, 0], K2[:, 0], L[:, 0]
