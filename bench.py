@@ -44,6 +44,11 @@ tests/golden/oracle_hashes.json.
 clock it runs at, and what vector instructions issued beside MFMAs cost
 (libserac_probe.so), the figures the sweep's bound is derived from.
 
+`--unfused` times the fused matcher against the unfused arm (the score
+matrix written to device memory, then row and column passes) on the 8192^2
+and 32768^2 workloads, with each arm's workspace: the analogue of the SERAC
+README's kernel-time and memory tables.
+
 `--f1-probe` bounds what reusing staged A tiles across the pairs of a batch
 could save: the fixed per-workgroup part of batch sweeps of 1 to 32 chunks.
 
@@ -244,6 +249,9 @@ def main() -> int:
                     help="instead of the benchmark, measure the int8 MFMA ceiling, the "
                          "shader clock and the issue cost of vector instructions beside "
                          "MFMAs (one JSON line)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="instead of the benchmark, time the fused matcher against the unfused "
+                         "arm (score matrix in memory) and report each arm's workspace")
     ap.add_argument("--f1-probe", action="store_true",
                     help="instead of the benchmark, bound what cross-pair reuse of A tiles in "
                          "a batch could save (one JSON line)")
@@ -295,6 +303,8 @@ def main() -> int:
         return all_configs(serac, synth, torch, np)
     if args.f1_probe:
         return f1_probe(serac, synth, torch, np)
+    if args.unfused:
+        return unfused_arm(serac, synth, torch, np)
     dev = torch.device("cuda:0")
     p = synth.workload(args.workload)
     nA, nB = p.A.shape[0], p.B.shape[0]
@@ -557,6 +567,56 @@ def host_pipeline(serac, synth, torch, np, reps: int = 5) -> int:
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def unfused_arm(serac, synth, torch, np, reps: int = 20) -> int:
+    """The fused matcher against the unfused arm (score matrix in device
+    memory, then row and column passes): time per pair and device memory of
+    each, on the 8192 x 8192 and 32768 x 32768 workloads, lists compared.
+    Each arm runs on a stream of its own, so each has its own workspace;
+    its size after the first call is the arm's device memory (the inputs
+    and the output list aside)."""
+    warm_device(serac, synth, torch)
+    res = {}
+    for name in ("pair_8192x8192", "pair_32768x32768"):
+        p = synth.workload(name)
+        prm = p.params()
+        a = torch.from_numpy(p.A).to("cuda:0")
+        b = torch.from_numpy(p.B).to("cuda:0")
+        nA = p.A.shape[0]
+        arms = {}
+        lists = {}
+        for arm, fn in (("fused", serac.match_pair_into),
+                        ("unfused", serac.match_pair_unfused_into)):
+            st = torch.cuda.Stream()
+            out = torch.empty((nA, 2), dtype=torch.int32, device="cuda:0")
+            cnt = torch.empty(1, dtype=torch.int32, device="cuda:0")
+            with torch.cuda.stream(st):
+                ws0 = serac.workspace_bytes()
+                fn(a, b, out, cnt, **prm)
+                st.synchronize()
+                ws = serac.workspace_bytes() - ws0
+                n = reps if nA <= 8192 else max(3, reps // 4)
+                t0 = time.perf_counter()
+                for _ in range(n):
+                    fn(a, b, out, cnt, **prm)
+                st.synchronize()
+                us = (time.perf_counter() - t0) / n * 1e6
+            lists[arm] = out[: int(cnt.item())].cpu().numpy().tobytes()
+            arms[arm] = {"us_per_pair": round(us, 2), "workspace_mib": round(ws / 2**20, 2)}
+        res[name] = {**arms, "speedup": round(arms["unfused"]["us_per_pair"] /
+                                              arms["fused"]["us_per_pair"], 2),
+                     "score_matrix_mib": round(nA * p.B.shape[0] * 4 / 2**20, 1),
+                     "identical": lists["fused"] == lists["unfused"]}
+    line = {
+        "metric": "fused matcher against the unfused arm: us per pair and workspace",
+        "value": res["pair_8192x8192"]["speedup"], "unit": "x (unfused / fused time)",
+        "higher_is_better": True, "n_gpus": 1, "reps": reps, "data": "synthetic",
+        "config": {"workloads": list(res)}, "arms": res,
+        "timing": "wall clock over back-to-back calls on one stream after the device warm-up",
+    }
+    print(json.dumps(line), flush=True)
+    return 0 if all(r["identical"] for r in res.values()) else 1
 
 
 def f1_probe(serac, synth, torch, np, reps: int = 7) -> int:

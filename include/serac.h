@@ -150,6 +150,21 @@ int serac_match_pair(const uint8_t *descA, int32_t nA, const uint8_t *descB,
                      const serac_matches *out_matches);
 
 /*
+ * The unfused arm, for comparison: the structure the SERAC README measures
+ * its fused kernel against ("GPU kernel time", "Memory").  The score matrix
+ * S is written to device memory (int32 [nA][nB]: the per-pair intermediate
+ * the README removes), then read back by a row pass (row top-2) and a column
+ * pass (column best); the finishing step is serac_match_pair's, so the list
+ * is the same, byte for byte.  Same arguments and errors as serac_match_pair,
+ * plus SERAC_ERR_TOO_LARGE above nA * nB = 2^32 (16 GiB of scores); the
+ * workspace grows by 4 * nA * nB bytes.  SERAC_FLAG_SYMMETRIC is refused
+ * (SERAC_ERR_INVALID_ARG); the match cap applies.
+ */
+int serac_match_pair_unfused(const uint8_t *descA, int32_t nA, const uint8_t *descB,
+                             int32_t nB, const serac_params *params,
+                             const serac_matches *out_matches);
+
+/*
  * Set up the current device for the library (architecture check, the angle
  * table, the fixed scratch of serac_match_pair_noalloc): the work every
  * other entry point does on its first call on a device, done now.  It

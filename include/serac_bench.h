@@ -55,6 +55,15 @@ int serac_profile_stop(double *tile_kernel_ms, int32_t *launches, float *per_lau
  */
 int serac_angle_slack(double *slack);
 
+/*
+ * Bytes of device memory the library's workspaces on the current device hold
+ * now (accumulators and scratch of every stream's workspace; not the angle
+ * table, the fixed scratch of serac_match_pair_noalloc, or pinned host
+ * memory).  Workspaces only grow, so after a call this is that call's peak.
+ * Errors: SERAC_ERR_INVALID_ARG (NULL), SERAC_ERR_HIP.
+ */
+int serac_workspace_bytes(int64_t *bytes);
+
 #ifdef __cplusplus
 }
 #endif

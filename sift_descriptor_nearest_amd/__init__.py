@@ -12,7 +12,8 @@ import math
 import os
 
 __all__ = ["match_pair", "match_pair_into", "match_pairs", "match_pairs_host", "top2",
-           "init", "match_pair_noalloc_into",
+           "init", "match_pair_noalloc_into", "match_pair_unfused", "match_pair_unfused_into",
+           "workspace_bytes",
            "profile_start", "profile_stop", "SeracError", "library", "LIB_PATH"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -80,6 +81,8 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          ctypes.POINTER(vp), ctypes.POINTER(i32)]
     L.serac_match_pair_noalloc.argtypes = L.serac_match_pair.argtypes
     L.serac_init.argtypes = []
+    L.serac_match_pair_unfused.argtypes = L.serac_match_pair.argtypes
+    L.serac_workspace_bytes.argtypes = [ctypes.POINTER(ctypes.c_int64)]
     L.serac_top2_pair.argtypes = [vp, i32, vp, i32, vp, vp, vp]
     L.serac_profile_start.argtypes = [i32, i32]
     L.serac_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32),
@@ -91,6 +94,7 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.serac_status_string.restype = ctypes.c_char_p
     for f in (L.serac_match_pair, L.serac_match_pairs, L.serac_match_pairs_host,
               L.serac_top2_pair, L.serac_init, L.serac_match_pair_noalloc,
+              L.serac_match_pair_unfused, L.serac_workspace_bytes,
               L.serac_profile_start, L.serac_profile_stop):
         f.restype = ctypes.c_int
     _lib = L
@@ -214,6 +218,49 @@ def match_pair(a, b, max_ratio=0.8, max_distance=math.inf, cross_check=True,
     if n < 0:
         raise SeracError(SERAC_ERR_HIP, "serac_match_pair: ordered output hand-off failed")
     return out[:n]
+
+
+def match_pair_unfused_into(a, b, out, count, max_ratio=0.8, max_distance=math.inf,
+                            cross_check=True, stream=None, max_features=0) -> None:
+    """match_pair_into through the unfused arm (serac_match_pair_unfused:
+    the score matrix written to device memory, then row and column passes).
+    Same result; for comparison.  Asynchronous like match_pair_into."""
+    _check_desc(a, "a")
+    _check_desc(b, "b")
+    if b.device != a.device:
+        raise ValueError("a and b must be on the same device")
+    _check_out(out, count, _capped(a.shape[0], max_features), a.device)
+    s = _stream(a.device) if stream is None else stream
+    p = _params(max_ratio, max_distance, cross_check, s, False, max_features)
+    m = serac_matches(out.data_ptr(), out.shape[0], count.data_ptr())
+    rc = library().serac_match_pair_unfused(a.data_ptr(), a.shape[0], b.data_ptr(), b.shape[0],
+                                            ctypes.byref(p), ctypes.byref(m))
+    if rc != SERAC_OK:
+        raise SeracError(rc, "serac_match_pair_unfused")
+
+
+def match_pair_unfused(a, b, max_ratio=0.8, max_distance=math.inf, cross_check=True,
+                       max_features=0):
+    """The list of match_pair_unfused_into as int32 [count, 2]; synchronises
+    the stream."""
+    import torch
+    out = torch.empty((max(a.shape[0], 1), 2), dtype=torch.int32, device=a.device)
+    count = torch.empty(1, dtype=torch.int32, device=a.device)
+    match_pair_unfused_into(a, b, out, count, max_ratio, max_distance, cross_check,
+                            max_features=max_features)
+    n = int(count.item())
+    if n < 0:
+        raise SeracError(SERAC_ERR_HIP, "serac_match_pair_unfused: ordered output hand-off failed")
+    return out[:n]
+
+
+def workspace_bytes() -> int:
+    """Device bytes the library's workspaces hold on the current device."""
+    v = ctypes.c_int64(0)
+    rc = library().serac_workspace_bytes(ctypes.byref(v))
+    if rc != SERAC_OK:
+        raise SeracError(rc, "serac_workspace_bytes")
+    return v.value
 
 
 def match_pairs(images, pairs, max_ratio=0.8, max_distance=math.inf,

@@ -1298,6 +1298,159 @@ __global__ void serac_export_cols(Job J, int32_t *col_best)
         J.cbest[j] = 0ull;
 }
 
+// ------------------------------------------------------------ unfused arm
+//
+// The structure the SERAC README measures its fused kernel against
+// ("GPU kernel time", "Memory"): the whole score matrix written to memory,
+// then separate row and column passes over it.  Here S (int32 [nA][nB],
+// the exact scores) is written by an MFMA kernel, read back by a row pass
+// (row top-2, one slot per row) and a column pass (column best, as the
+// sweep's atomic maxima leave it), and the finishing kernel does the rest,
+// so its lists equal the fused path's.  It is a comparison arm: its memory
+// grows as nA * nB and every score crosses HBM three times.
+
+constexpr long long UNFUSED_MAX_SCORES = 1ll << 32;   // nA * nB (16 GiB of scores)
+constexpr int SCORE_ROWS = 128;        // rows of A per workgroup (4 waves x 32)
+constexpr int SCORE_COLS = 256;        // columns of B per workgroup (8 tiles of 32)
+constexpr int SCORE_THREADS = 256;
+
+// S[i][j] for a 128 x 256 block: each wave holds the operand fragments of
+// its 32 rows (lane (n, h): bytes [32 kc + 16 h, +16) of row n) and sweeps
+// eight 32-column tiles, reading B's fragments straight from memory; the
+// row term enters as the MFMA's C input and the column term is added before
+// the store.  Rows and columns past the sets read the zero descriptor and
+// are not stored.
+__global__ __launch_bounds__(SCORE_THREADS) void serac_scores(const uint8_t *A, const uint8_t *B,
+                                                              int32_t nA, int32_t nB, int32_t *S)
+{
+    __shared__ int32_t sRT[SCORE_ROWS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, h = lane >> 5;
+    const int row0 = blockIdx.y * SCORE_ROWS + w * WAVE_ROWS;
+    const int col0 = blockIdx.x * SCORE_COLS;
+
+    const int ra = row0 + n;
+    const uint8_t *pa = (ra < nA ? A + (size_t)ra * DIM : g_zero_desc) + 16 * h;
+    v4i af[4];
+    uint32_t sa = 0u;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+        const uint4 v = load_global16(pa + 32 * kc);
+        sa += bytesum16(v);
+        af[kc] = (v4i){(int)(v.x ^ 0x80808080u), (int)(v.y ^ 0x80808080u),
+                       (int)(v.z ^ 0x80808080u), (int)(v.w ^ 0x80808080u)};
+    }
+    sa += __shfl_xor(sa, 32);
+    if (h == 0)
+        sRT[w * WAVE_ROWS + n] = (int32_t)(128u * sa) - 2097152;
+    __syncthreads();
+    // C input: register r of lane half h is output row (r / 4) * 8 + h * 4 + r % 4
+    v16i ci;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        ci[r] = sRT[w * WAVE_ROWS + (r >> 2) * 8 + h * 4 + (r & 3)];
+
+    for (int t = 0; t < SCORE_COLS / 32; ++t) {
+        const int cb = col0 + 32 * t + n;
+        const uint8_t *pb = (cb < nB ? B + (size_t)cb * DIM : g_zero_desc) + 16 * h;
+        v4i bf[4];
+        uint32_t sb = 0u;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            const uint4 v = load_global16(pb + 32 * kc);
+            sb += bytesum16(v);
+            bf[kc] = (v4i){(int)(v.x ^ 0x80808080u), (int)(v.y ^ 0x80808080u),
+                           (int)(v.z ^ 0x80808080u), (int)(v.w ^ 0x80808080u)};
+        }
+        sb += __shfl_xor(sb, 32);
+        v16i acc = ci;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[kc], bf[kc], acc, 0, 0, 0);
+        if (cb < nB) {
+            const int32_t colterm = (int32_t)(128u * sb);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = row0 + (r >> 2) * 8 + h * 4 + (r & 3);
+                if (i < nA)
+                    S[(size_t)i * nB + cb] = acc[r] + colterm;
+            }
+        }
+    }
+}
+
+// Row pass: one workgroup per row, its threads over the columns in
+// ascending steps; each keeps the top two of the 64-bit keys
+// (S << 32 | ~j) (largest score, then lowest column; a tie leaves the tied
+// score second), merged across the workgroup the same way.  The row's
+// result goes out as the single slot of one column group.
+__global__ __launch_bounds__(256) void serac_score_rows(const int32_t *S, int32_t nA, int32_t nB,
+                                                        unsigned long long *rslot)
+{
+    __shared__ unsigned long long sK[2][256 / 64];
+    const int i = blockIdx.x;
+    const int32_t *row = S + (size_t)i * nB;
+    unsigned long long k1 = 0ull, k2 = 0ull;
+#pragma unroll 8
+    for (int j = threadIdx.x; j < nB; j += 256) {
+        const unsigned long long k =
+            ((unsigned long long)(uint32_t)row[j] << 32) | (0xFFFFFFFFu - (uint32_t)j);
+        k2 = max(k2, min(k1, k));
+        k1 = max(k1, k);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        const unsigned long long o1 = __shfl_xor(k1, d), o2 = __shfl_xor(k2, d);
+        k2 = max(max(k2, o2), min(k1, o1));
+        k1 = max(k1, o1);
+    }
+    const int wv = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        sK[0][wv] = k1;
+        sK[1][wv] = k2;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        k1 = sK[0][0];
+        k2 = sK[1][0];
+        for (int v = 1; v < 256 / 64; ++v) {
+            k2 = max(max(k2, sK[1][v]), min(k1, sK[0][v]));
+            k1 = max(k1, sK[0][v]);
+        }
+        const uint32_t S1 = (uint32_t)(k1 >> 32), S2 = (uint32_t)(k2 >> 32);
+        const uint32_t col = 0xFFFFFFFFu - (uint32_t)k1;
+        rslot[i] = pack_slot(S1, col, S2);
+    }
+}
+
+// Column pass: a thread per column over a band of rows in ascending order
+// (consecutive threads read consecutive columns of a row); the band's best
+// goes to the column bests as the sweep leaves them, (S << 32) | ~slice
+// raised by an atomic maximum (highest score, then lowest 16-row slice).
+constexpr int SCORE_BAND = 512;        // rows per column-pass workgroup
+
+__global__ __launch_bounds__(256) void serac_score_cols(const int32_t *S, int32_t nA, int32_t nB,
+                                                        unsigned long long *cbest)
+{
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= nB)
+        return;
+    const int i0 = blockIdx.y * SCORE_BAND, i1 = min(i0 + SCORE_BAND, nA);
+    int32_t best = 0, at = -1;
+#pragma unroll 16
+    for (int i = i0; i < i1; ++i) {
+        const int32_t v = S[(size_t)i * nB + j];
+        if (v > best) {
+            best = v;
+            at = i;
+        }
+    }
+    if (at >= 0)
+        atomicMax(cbest + j, ((unsigned long long)(uint32_t)best << 32) |
+                                 (0xFFFFFFFFu - (uint32_t)(at / SLICE)));
+}
+
 
 // ------------------------------------------------------------------ host
 
@@ -2571,6 +2724,96 @@ int serac_match_pairs_host(const uint8_t *const *desc, const int32_t *n, int32_t
                 rc = SERAC_ERR_HIP;
         }
         return rc;
+    });
+}
+
+int serac_match_pair_unfused(const uint8_t *descA, int32_t nA, const uint8_t *descB,
+                             int32_t nB, const serac_params *params, const serac_matches *out)
+{
+    return guarded([&]() -> int {
+        if (bad_set(descA, nA) || bad_set(descB, nB) || bad_params(params) || !out ||
+            symmetric(params))
+            return SERAC_ERR_INVALID_ARG;
+        nA = capped(nA, params);
+        nB = capped(nB, params);
+        if (bad_out(*out, nA))
+            return SERAC_ERR_INVALID_ARG;
+        if (out->capacity < nA)
+            return SERAC_ERR_CAPACITY;
+        if ((long long)nA * nB > UNFUSED_MAX_SCORES)
+            return SERAC_ERR_TOO_LARGE;
+        Device *d = nullptr;
+        int st = device_setup(&d);
+        if (st != SERAC_OK)
+            return st;
+        hipStream_t stream = static_cast<hipStream_t>(params->stream);
+        if (nA == 0 || nB == 0) {
+            serac_zero_counts<<<1, 64, 0, stream>>>(nullptr, out->count, 1);
+            return hipGetLastError() == hipSuccess ? SERAC_OK : SERAC_ERR_HIP;
+        }
+        // accumulators: column bests (64-bit) and finishing status words;
+        // scratch: the score matrix, then one slot per row
+        const size_t gates = (size_t)(nA + GATE_THREADS - 1) / GATE_THREADS;
+        const size_t acc = align256((size_t)nB * 8) + align256(gates * 8);
+        const size_t sbytes = align256((size_t)nA * nB * 4);
+        Workspace *w = nullptr;
+        std::unique_lock<std::mutex> hold;
+        st = get_workspace(stream, acc, sbytes + align256((size_t)nA * 8), &w, hold);
+        if (st != SERAC_OK)
+            return st;
+        uint8_t *const region = next_region(w);
+        const Clear C = take_clear(w, acc);
+        if (C.words)
+            serac_clear<<<(unsigned)std::min<size_t>((C.words + 255) / 256, 1024), 256, 0,
+                          stream>>>(C.p, C.words);
+        int32_t *S = reinterpret_cast<int32_t *>(w->aux);
+        unsigned long long *rslot = reinterpret_cast<unsigned long long *>(w->aux + sbytes);
+        unsigned long long *cbest = reinterpret_cast<unsigned long long *>(region);
+        serac_scores<<<dim3((nB + SCORE_COLS - 1) / SCORE_COLS, (nA + SCORE_ROWS - 1) / SCORE_ROWS),
+                       SCORE_THREADS, 0, stream>>>(descA, descB, nA, nB, S);
+        serac_score_rows<<<nA, 256, 0, stream>>>(S, nA, nB, rslot);
+        if (params->cross_check)
+            serac_score_cols<<<dim3((nB + 255) / 256, (nA + SCORE_BAND - 1) / SCORE_BAND), 256, 0,
+                               stream>>>(S, nA, nB, cbest);
+        Job J;
+        J.A = descA;
+        J.B = descB;
+        J.nA = nA;
+        J.nB = nB;
+        J.Gc = 1;
+        J.rslot = rslot;
+        J.rs1 = nullptr;
+        J.cbest = cbest;
+        J.cb32 = 0;
+        J.status = reinterpret_cast<unsigned long long *>(region + align256((size_t)nB * 8));
+        J.out = out->matches;
+        J.count = out->count;
+        const Gate G = make_gate(d, params);
+        serac_finish_one<false><<<(nA + GATE_THREADS - 1) / GATE_THREADS, GATE_THREADS, 0, stream>>>(
+            J.rslot, J.nA, J.nB, J.Gc, J.cbest, G.table, G.cross_check, J, G);
+        if (hipGetLastError() != hipSuccess) {
+            mark_dirty(w);
+            return SERAC_ERR_HIP;
+        }
+        return SERAC_OK;
+    });
+}
+
+int serac_workspace_bytes(int64_t *bytes)
+{
+    return guarded([&]() -> int {
+        if (!bytes)
+            return SERAC_ERR_INVALID_ARG;
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess)
+            return hip_fail();
+        size_t total = 0;
+        std::lock_guard<std::mutex> lock(g_ws_mutex);
+        for (auto &e : g_ws)
+            if (e.dev == dev)
+                total += e.acc_bytes + e.aux_bytes;
+        *bytes = (int64_t)total;
+        return SERAC_OK;
     });
 }
 

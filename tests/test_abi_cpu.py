@@ -25,7 +25,8 @@ def test_library_exports_every_declared_function():
     L = serac.library()
     names = declared() + declared(os.path.join(ROOT, "include", "serac_bench.h"))
     assert {"serac_match_pair", "serac_match_pairs", "serac_top2_pair",
-            "serac_init", "serac_match_pair_noalloc", "serac_status_string", "serac_profile_start", "serac_profile_stop",
+            "serac_init", "serac_match_pair_noalloc", "serac_match_pair_unfused",
+            "serac_workspace_bytes", "serac_status_string", "serac_profile_start", "serac_profile_stop",
             "serac_angle_slack"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
@@ -134,6 +135,24 @@ def test_match_pair_noalloc_validation():
     assert call(nA=16385, nB=16385, out=big) == serac.SERAC_ERR_TOO_LARGE
     assert call(nA=1, nB=(1 << 28) + 1, out=big) == serac.SERAC_ERR_INVALID_ARG   # > max set
     assert call(nA=2048, nB=131073, out=big) == serac.SERAC_ERR_TOO_LARGE
+
+
+def test_match_pair_unfused_validation():
+    L = serac.library()
+    E = serac.SERAC_ERR_INVALID_ARG
+
+    def call(a=FAKE, nA=10, b=FAKE, nB=10, params=None, out=None):
+        return L.serac_match_pair_unfused(a, nA, b, nB, ctypes.byref(params or _p()),
+                                          ctypes.byref(out or _m()))
+
+    assert call(a=None) == E
+    assert call(b=FAKE + 4) == E
+    assert call(params=_p(flags=serac.SERAC_FLAG_SYMMETRIC)) == E
+    assert call(params=_p(cross_check=3)) == E
+    assert call(nA=101) == serac.SERAC_ERR_CAPACITY
+    big = serac_matches(FAKE, 1 << 20, FAKE)
+    assert call(nA=65537, nB=65537, out=big) == serac.SERAC_ERR_TOO_LARGE
+    assert L.serac_workspace_bytes(None) == E
 
 
 def test_match_pair_rejects_small_capacity():
