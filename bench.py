@@ -49,6 +49,10 @@ matrix written to device memory, then row and column passes) on the 8192^2
 and 32768^2 workloads, with each arm's workspace: the analogue of the SERAC
 README's kernel-time and memory tables.
 
+`--clock-ramp` records the shader clock and the step time against the
+number of back-to-back steps from a cold start (why the default run warms
+up for 2000 steps).
+
 `--f1-probe` bounds what reusing staged A tiles across the pairs of a batch
 could save: the fixed per-workgroup part of batch sweeps of 1 to 32 chunks.
 
@@ -252,6 +256,9 @@ def main() -> int:
     ap.add_argument("--unfused", action="store_true",
                     help="instead of the benchmark, time the fused matcher against the unfused "
                          "arm (score matrix in memory) and report each arm's workspace")
+    ap.add_argument("--clock-ramp", action="store_true",
+                    help="instead of the benchmark, record the shader clock and the step time "
+                         "against the number of back-to-back steps from a cold start")
     ap.add_argument("--f1-probe", action="store_true",
                     help="instead of the benchmark, bound what cross-pair reuse of A tiles in "
                          "a batch could save (one JSON line)")
@@ -303,6 +310,8 @@ def main() -> int:
         return all_configs(serac, synth, torch, np)
     if args.f1_probe:
         return f1_probe(serac, synth, torch, np)
+    if args.clock_ramp:
+        return clock_ramp(serac, synth, torch, np)
     if args.unfused:
         return unfused_arm(serac, synth, torch, np)
     dev = torch.device("cuda:0")
@@ -617,6 +626,38 @@ def unfused_arm(serac, synth, torch, np, reps: int = 20) -> int:
     }
     print(json.dumps(line), flush=True)
     return 0 if all(r["identical"] for r in res.values()) else 1
+
+
+def clock_ramp(serac, synth, torch, np) -> int:
+    """How the shader clock and the step time of the 8192 x 8192 benchmark
+    grow with back-to-back steps from a cold start: at each checkpoint, 20
+    steps timed by wall clock, then the clock the int8 MFMA probe's waves
+    see (libserac_probe.so, a ~15 us launch)."""
+    p = synth.workload("pair_8192x8192")
+    a = torch.from_numpy(p.A).to("cuda:0")
+    b = torch.from_numpy(p.B).to("cuda:0")
+    out = torch.empty((8192, 2), dtype=torch.int32, device="cuda:0")
+    cnt = torch.empty(1, dtype=torch.int32, device="cuda:0")
+    prm = p.params()
+    torch.cuda.synchronize()
+    done, pts = 0, []
+    for cp in (0, 5, 25, 100, 300, 1000, 2000, 4000, 7000):
+        for _ in range(cp - done):
+            serac.match_pair_into(a, b, out, cnt, **prm)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(20):
+            serac.match_pair_into(a, b, out, cnt, **prm)
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) / 20 * 1e6
+        _, _, ghz = serac.probe_mfma(256, 300, 0)
+        done = cp + 20
+        pts.append({"steps_before": cp, "us_per_step": round(us, 2), "shader_ghz": round(ghz, 3)})
+    line = {"metric": "shader clock and 8192 x 8192 step time against back-to-back steps",
+            "value": pts[-1]["shader_ghz"], "unit": "GHz after 7000 steps",
+            "higher_is_better": True, "n_gpus": 1, "data": "synthetic", "ramp": pts}
+    print(json.dumps(line), flush=True)
+    return 0
 
 
 def f1_probe(serac, synth, torch, np, reps: int = 7) -> int:
