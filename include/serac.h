@@ -165,6 +165,19 @@ int serac_match_pair_unfused(const uint8_t *descA, int32_t nA, const uint8_t *de
                              const serac_matches *out_matches);
 
 /*
+ * Release the current device's workspace for `stream` (device scratch and
+ * pinned staging memory the library keeps per stream; NULL = the null
+ * stream), e.g. before destroying a stream that will not be used again.
+ * Device memory is freed in stream order behind the work already enqueued
+ * on `stream`; the call waits for the copies out of the pinned staging
+ * memory that are still pending.  A later call on the stream allocates a
+ * new workspace.  No-op if the stream has none.  Must not overlap a call on
+ * the same stream from another thread.
+ * Errors: SERAC_ERR_HIP.
+ */
+int serac_release_stream(void *stream);
+
+/*
  * Set up the current device for the library (architecture check, the angle
  * table, the fixed scratch of serac_match_pair_noalloc): the work every
  * other entry point does on its first call on a device, done now.  It

@@ -13,7 +13,7 @@ import os
 
 __all__ = ["match_pair", "match_pair_into", "match_pairs", "match_pairs_host", "top2",
            "init", "match_pair_noalloc_into", "match_pair_unfused", "match_pair_unfused_into",
-           "workspace_bytes",
+           "workspace_bytes", "release_stream",
            "profile_start", "profile_stop", "SeracError", "library", "LIB_PATH"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -83,6 +83,7 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.serac_init.argtypes = []
     L.serac_match_pair_unfused.argtypes = L.serac_match_pair.argtypes
     L.serac_workspace_bytes.argtypes = [ctypes.POINTER(ctypes.c_int64)]
+    L.serac_release_stream.argtypes = [vp]
     L.serac_top2_pair.argtypes = [vp, i32, vp, i32, vp, vp, vp]
     L.serac_profile_start.argtypes = [i32, i32]
     L.serac_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32),
@@ -94,7 +95,7 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.serac_status_string.restype = ctypes.c_char_p
     for f in (L.serac_match_pair, L.serac_match_pairs, L.serac_match_pairs_host,
               L.serac_top2_pair, L.serac_init, L.serac_match_pair_noalloc,
-              L.serac_match_pair_unfused, L.serac_workspace_bytes,
+              L.serac_match_pair_unfused, L.serac_workspace_bytes, L.serac_release_stream,
               L.serac_profile_start, L.serac_profile_stop):
         f.restype = ctypes.c_int
     _lib = L
@@ -252,6 +253,17 @@ def match_pair_unfused(a, b, max_ratio=0.8, max_distance=math.inf, cross_check=T
     if n < 0:
         raise SeracError(SERAC_ERR_HIP, "serac_match_pair_unfused: ordered output hand-off failed")
     return out[:n]
+
+
+def release_stream(stream=None, device=None) -> None:
+    """Free the library's workspace for a stream (default: torch's current
+    stream on `device`); a later call on it allocates a new one."""
+    import torch
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    s = _stream(dev) if stream is None else stream
+    rc = library().serac_release_stream(ctypes.c_void_p(s))
+    if rc != SERAC_OK:
+        raise SeracError(rc, "serac_release_stream")
 
 
 def workspace_bytes() -> int:

@@ -1710,6 +1710,7 @@ struct Workspace {
     hipEvent_t staged[STAGE_RING] = {};   // recorded after the copy out of stage[k] (or null)
     int stage_next = 0;                   // the ring entry the next batch call uses
     std::mutex busy;                 // held by the call enqueueing on this workspace
+    bool released = false;           // freed by serac_release_stream; free for reuse
 };
 std::mutex g_ws_mutex;          // guards the list itself
 std::deque<Workspace> g_ws;     // a deque: workspaces keep their addresses as others are added
@@ -1750,8 +1751,20 @@ int get_workspace(hipStream_t stream, size_t acc_bytes, size_t aux_bytes, Worksp
     {
         std::lock_guard<std::mutex> lock(g_ws_mutex);
         for (auto &e : g_ws)
-            if (e.dev == dev && e.stream == stream)
+            if (!e.released && e.dev == dev && e.stream == stream)
                 w = &e;
+        // a released entry is reused for a new stream (the list never shrinks:
+        // entries keep their addresses)
+        for (auto &e : g_ws)
+            if (!w && e.released && e.busy.try_lock()) {
+                if (e.released) {
+                    e.released = false;
+                    e.dev = dev;
+                    e.stream = stream;
+                    w = &e;
+                }
+                e.busy.unlock();
+            }
         if (!w) {
             w = &g_ws.emplace_back();
             w->dev = dev;
@@ -2799,6 +2812,58 @@ int serac_match_pair_unfused(const uint8_t *descA, int32_t nA, const uint8_t *de
     });
 }
 
+int serac_release_stream(void *stream_)
+{
+    return guarded([&]() -> int {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess)
+            return hip_fail();
+        hipStream_t stream = static_cast<hipStream_t>(stream_);
+        Workspace *w = nullptr;
+        {
+            std::lock_guard<std::mutex> lock(g_ws_mutex);
+            for (auto &e : g_ws)
+                if (!e.released && e.dev == dev && e.stream == stream)
+                    w = &e;
+        }
+        if (!w)
+            return SERAC_OK;
+        std::lock_guard<std::mutex> hold(w->busy);
+        int st = SERAC_OK;
+        // device buffers: freed in stream order, behind the work that uses them
+        if (w->acc && hipFreeAsync(w->acc, stream) != hipSuccess)
+            st = SERAC_ERR_HIP;
+        if (w->aux && hipFreeAsync(w->aux, stream) != hipSuccess)
+            st = SERAC_ERR_HIP;
+        // pinned staging: freed once the copies out of it have run
+        for (int k = 0; k < STAGE_RING; ++k) {
+            if (w->staged[k]) {
+                if (hipEventSynchronize(w->staged[k]) != hipSuccess)
+                    st = SERAC_ERR_HIP;
+                (void)hipEventDestroy(w->staged[k]);
+            }
+            if (w->stage[k])
+                (void)hipHostFree(w->stage[k]);
+            w->staged[k] = nullptr;
+            w->stage[k] = nullptr;
+            w->stage_bytes[k] = 0;
+        }
+        (void)hipGetLastError();
+        w->acc = w->aux = nullptr;
+        w->acc_bytes = w->aux_bytes = 0;
+        w->acc_used[0] = w->acc_used[1] = 0;
+        w->region = 0;
+        w->dirty = false;
+        w->stage_next = 0;
+        {
+            std::lock_guard<std::mutex> lock(g_ws_mutex);
+            w->released = true;
+            w->stream = nullptr;
+        }
+        return st;
+    });
+}
+
 int serac_workspace_bytes(int64_t *bytes)
 {
     return guarded([&]() -> int {
@@ -2810,7 +2875,7 @@ int serac_workspace_bytes(int64_t *bytes)
         size_t total = 0;
         std::lock_guard<std::mutex> lock(g_ws_mutex);
         for (auto &e : g_ws)
-            if (e.dev == dev)
+            if (e.dev == dev && !e.released)
                 total += e.acc_bytes + e.aux_bytes;
         *bytes = (int64_t)total;
         return SERAC_OK;

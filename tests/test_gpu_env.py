@@ -120,3 +120,37 @@ assert res[0].cpu().numpy().astype(np.uint32).tobytes() == oracle.match_pair(p.A
 print("ok batch after failure", flush=True)
 """
     run(code, {"SERAC_TEST_FAIL_ALLOC": "1"})
+
+
+def test_release_stream(gpu):
+    """Workspaces of side streams are freed by serac_release_stream and
+    come back on the next call; results stay the oracle's."""
+    code = """
+p = synth.workload("pair_1000x1200")
+a, b = dev(p.A), dev(p.B)
+want = oracle.match_pair(p.A, p.B, 0.8, math.inf, True)
+serac.match_pair(a, b)                        # the null stream's workspace
+base = serac.workspace_bytes()
+streams = [torch.cuda.Stream() for _ in range(3)]
+for s in streams:
+    with torch.cuda.stream(s):
+        assert serac.match_pair(a, b).cpu().numpy().astype(np.uint32).tobytes() == want.tobytes()
+grown = serac.workspace_bytes()
+assert grown > base, (grown, base)
+for s in streams:
+    serac.release_stream(s.cuda_stream)
+    serac.release_stream(s.cuda_stream)       # a second release is a no-op
+assert serac.workspace_bytes() == base, (serac.workspace_bytes(), base)
+for s in streams:                             # released entries are reused
+    with torch.cuda.stream(s):
+        assert serac.match_pair(a, b).cpu().numpy().astype(np.uint32).tobytes() == want.tobytes()
+imgs = [a, b]
+with torch.cuda.stream(streams[0]):
+    r = serac.match_pairs(imgs, [(0, 1), (1, 0)])
+    serac.release_stream(streams[0].cuda_stream)
+    assert r[0].cpu().numpy().astype(np.uint32).tobytes() == want.tobytes()
+torch.cuda.synchronize()
+print("ok release", base, grown, flush=True)
+"""
+    run(code, {})
+
