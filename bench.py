@@ -505,7 +505,27 @@ def all_configs(serac, synth, torch, np) -> int:
         got = out[: int(cnt.item())].cpu().numpy().astype(np.uint32)
         same = bool(list_sha(got) == want["sha256"] and len(got) == want["count"])
         ok = ok and same
-        emit(name, nA, nB, us, ops, same, int(len(got)), calls=reps, **prm)
+        # the dominant kernel's own time: 16 further calls, each tile launch
+        # event-timed
+        serac.profile_start(16, 1)
+        for _ in range(16):
+            serac.match_pair_into(a, b, out, cnt, **prm)
+        torch.cuda.synchronize()
+        _, n, per, kname = serac.profile_stop()
+        extra = {"tile_kernel": kname, "tile_us_mean": round(1e3 * float(np.mean(per)), 3),
+                 "tile_us_median": round(1e3 * float(np.median(per)), 3), "tile_launches": n,
+                 "tile_frac": round(ops / (1e-3 * float(np.mean(per))) / 1e12 / PEAK_INT8_TOPS, 4)}
+        if nA * nB <= 8192 * 8192:
+            # the oracle's time for the same list, on this host's cores
+            import oracle
+            t0 = time.perf_counter()
+            ref = oracle.match_pair(p.A, p.B, **prm)
+            extra.update({"oracle_s": round(time.perf_counter() - t0, 3),
+                          "oracle_cores": oracle.max_threads(),
+                          "oracle_identical": bool(ref.tobytes() == got.tobytes())})
+            ok = ok and extra["oracle_identical"]
+        emit(name, nA, nB, us, ops, same, int(len(got)), calls=reps,
+             inputs_sha256=synth.sha256(p.A, p.B), list_sha256=list_sha(got), **extra, **prm)
 
     bt = synth.exhaustive_48x8192()
     want = G["batch"][bt.name]

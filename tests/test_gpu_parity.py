@@ -224,6 +224,32 @@ def test_determinism_and_stream(serac):
     assert outs[0] == want.tobytes()
 
 
+def test_pipelined_calls_identical(serac):
+    """30 calls in flight on one stream with no synchronisation between
+    them, alternating three pairs of different shapes and paths (fused
+    32-bit, fused 64-bit column bests, prepared), each into its own output:
+    every list is the oracle's.  Consecutive calls share the workspace's
+    accumulator regions (each call clears what the one before left), so a
+    race between calls would show here (the pages' 30 pipelined frames)."""
+    cases = [synth.workload("edge_8192x8192_ties_no255"),
+             synth.pair(9000, 5000, 0.2, 4, seed=6),         # > 8192 rows: 64-bit column bests
+             synth.pair(16385, 16384, 0.1, 4, seed=7)]       # > 2^28 products: prepared sets
+    dv = [(dev(c.A), dev(c.B)) for c in cases]
+    want = [oracle.match_pair(c.A, c.B, 0.8, math.inf, True).tobytes() for c in cases]
+    outs = []
+    torch.cuda.synchronize()
+    for k in range(30):
+        a, b = dv[k % 3]
+        out = torch.full((a.shape[0], 2), -1, dtype=torch.int32, device="cuda:0")
+        cnt = torch.full((1,), -7, dtype=torch.int32, device="cuda:0")
+        serac.match_pair_into(a, b, out, cnt)
+        outs.append((out, cnt))
+    torch.cuda.synchronize()
+    for k, (out, cnt) in enumerate(outs):
+        got = out[: int(cnt.item())].cpu().numpy().tobytes()
+        assert got == want[k % 3], k
+
+
 def test_workload_pair_32768_sampled(serac):
     p = synth.workload("pair_32768x32768")
     a, b = dev(p.A), dev(p.B)
