@@ -21,7 +21,7 @@ that is fewer than MIN_TIMED_LAUNCHES (a short run), back-to-back steps
 right after the timed region with every launch timed, up to that many.  Under rocprofv3 these readings are not meaningful (the profiler
 takes over the dispatch timestamps), so there the profiler's own kernel
 trace is the measurement.  `traffic` is the HBM bytes per launch from the
-committed counter runs of this command, null once the kernel has changed.
+committed counter runs of this command, null once the device code has changed.
 `cpu_baseline` is the oracle on this host's cores, timed on a bounded
 number of full-pair runs, with the CPU model and the single-thread time of
 the 1000 x 1200 and 8192 x 8192 pairs.  `sha256` holds the inputs' and the
@@ -86,15 +86,32 @@ MIN_TIMED_LAUNCHES = 16
 # The headline workload's metric, worded as the benchmark's own definition.
 METRIC_8192 = "int8 TOPS and ms/pair, 8192\u00d78192\u00d7128 uint8 pair; % of MFMA int8 peak"
 TRAFFIC = os.path.join(ROOT, "profiles", "traffic_tiles_pair_8192x8192.json")
-KERNEL_SRC = os.path.join(ROOT, "sift_descriptor_nearest_amd", "csrc", "serac.hip")
 
 
 def kernel_sha() -> str:
-    """sha256 of the kernel source and the compiler flags it is built with."""
-    from sift_descriptor_nearest_amd.build import HIPCC_FLAGS
-    with open(KERNEL_SRC, "rb") as f:
-        src = f.read()
-    return hashlib.sha256(src + b"\0" + " ".join(HIPCC_FLAGS).encode()).hexdigest()
+    """sha256 of the device code the benchmark runs: the gfx950 code object
+    embedded in the library (its .hip_fatbin section).  Host-only and
+    comment changes leave it alone; any change to a kernel or to the device
+    compilation changes it."""
+    import struct
+    from sift_descriptor_nearest_amd import LIB_PATH
+    with open(LIB_PATH, "rb") as f:
+        d = f.read()
+    if d[:4] != b"\x7fELF" or d[4] != 2:
+        raise RuntimeError(f"{LIB_PATH} is not a 64-bit ELF library")
+    shoff = struct.unpack_from("<Q", d, 0x28)[0]
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", d, 0x3A)
+
+    def header(i):
+        return struct.unpack_from("<IIQQQQ", d, shoff + i * shentsize)
+
+    names = header(shstrndx)[4]
+    for i in range(shnum):
+        name, _, _, _, off, size = header(i)
+        end = d.index(b"\0", names + name)
+        if d[names + name:end] == b".hip_fatbin":
+            return hashlib.sha256(d[off:off + size]).hexdigest()
+    raise RuntimeError(f"{LIB_PATH} holds no .hip_fatbin section")
 
 
 def measured_traffic():

@@ -59,14 +59,22 @@
 //   * All merges (across lanes, waves, workgroups) compare packed keys or
 //     scan in ascending index order, so the result does not depend on
 //     scheduling (MASDA part 3, section 6: an order-independent key).
-//   * The angle gate reads a table of acos(s / 512^2) built on the host with
-//     the C library's acos, so the double-precision decision is the same
-//     one a CPU makes; the ratio test is one IEEE multiply and compare.
+//   * The angle gates take the C library's acos of s / 512^2 (a table built
+//     on the host), so each double-precision decision is the one a CPU
+//     makes; a single pair's finishing kernel first evaluates the device's
+//     own acos and trusts it only where a bracket measured against the
+//     table at set-up settles the decision.  The ratio test is one IEEE
+//     multiply and compare.
+//   * Variants: symmetric column gates run the sweep of the swapped pair as
+//     well and compare each row's best column's accepted row; the match cap
+//     takes the first descriptors of each set; an unfused comparison arm
+//     writes the score matrix and reduces it in separate passes; a
+//     non-allocating entry point works in a fixed device array.
 //   * Host side: one workspace per (device, stream), grow-only and
-//     stream-ordered; a batch stages its job tables through pinned memory
-//     behind an event; serac_match_pairs_host runs a batch in stages and
-//     overlaps the copy of each stage's lists to the host with the
-//     matching of the next.
+//     stream-ordered, releasable per stream; a batch stages its job tables
+//     through a ring of pinned buffers, each behind an event;
+//     serac_match_pairs_host runs a batch in stages and overlaps the copy of
+//     each stage's lists to the host with the matching of the next.
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
