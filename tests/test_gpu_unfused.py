@@ -92,3 +92,23 @@ def test_workload_8192_digest(serac):
         assert len(got) == want["count"]
         assert hashlib.sha256(got.tobytes()).hexdigest() == want["sha256"], key
     assert serac.workspace_bytes() >= 8192 * 8192 * 4
+
+
+def test_past_2_31_scores(serac):
+    """65536 x 65536 (2^32 scores, the arm's limit): every int32 index of S
+    past 2^31 is formed in 64 bits; the list equals the fused path's, which
+    the oracle pins at every size below (and by its digests at 32768^2)."""
+    p = synth.pair(65536, 65536, 0.05, 4, seed=12)
+    a, b = dev(p.A), dev(p.B)
+    say("[unfused] 65536 x 65536")
+    got = serac.match_pair_unfused(a, b, 0.8, math.inf, True).cpu().numpy()
+    ref = serac.match_pair(a, b, 0.8, math.inf, True).cpu().numpy()
+    assert len(got) > 3000
+    assert got.tobytes() == ref.tobytes()
+    # a sample of rows settled by the oracle one by one
+    rows = np.linspace(0, 65535, 48).astype(np.int32)
+    want = oracle.match_rows(p.A, p.B, rows, 0.8)
+    have = {int(i): int(j) for i, j in got.tolist()}
+    for i, j in want.items():
+        assert have.get(i, -1) == j, i
+    serac.release_stream()                        # give the 16 GiB back
