@@ -56,6 +56,12 @@ up for 2000 steps).
 `--f1-probe` bounds what reusing staged A tiles across the pairs of a batch
 could save: the fixed per-workgroup part of batch sweeps of 1 to 32 chunks.
 
+`--strips` times exhaustive image sets of 512 to 10400 descriptors per
+image with the pairs swept one by one, in strips of up to 16 pairs that
+share their A image (cross-pair reuse), and as the library chooses, each in
+a child process (the library reads the setting at start-up), and checks
+that the lists are identical.
+
 `--copy-probe MIB` and `--write-traffic DIR` make the traffic record: the
 first runs a plain copy of known size for the counter scales, the second
 (on any host) turns four rocprofv3 FETCH_SIZE / WRITE_SIZE runs into
@@ -68,6 +74,7 @@ import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -279,6 +286,12 @@ def main() -> int:
     ap.add_argument("--f1-probe", action="store_true",
                     help="instead of the benchmark, bound what cross-pair reuse of A tiles in "
                          "a batch could save (one JSON line)")
+    ap.add_argument("--strips", action="store_true",
+                    help="instead of the benchmark, time exhaustive image sets of several "
+                         "image sizes with pairs swept one by one, in strips of pairs that "
+                         "share their A image, and as the library chooses (one JSON line)")
+    ap.add_argument("--strips-child", type=int, default=0, metavar="REPS",
+                    help=argparse.SUPPRESS)
     ap.add_argument("--write-traffic", metavar="DIR",
                     help="on any host: write the traffic record from the four rocprofv3 "
                          "--pmc runs under DIR/{fetch,write,copy_fetch,copy_write}")
@@ -300,6 +313,8 @@ def main() -> int:
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be at least 1 and --warmup at least 0", file=sys.stderr)
         return 2
+    if args.strips:
+        return strips_compare()
 
     import numpy as np
     import torch
@@ -331,6 +346,8 @@ def main() -> int:
         return clock_ramp(serac, synth, torch, np)
     if args.unfused:
         return unfused_arm(serac, synth, torch, np)
+    if args.strips_child:
+        return strips_child(serac, synth, torch, np, args.strips_child)
     dev = torch.device("cuda:0")
     p = synth.workload(args.workload)
     nA, nB = p.A.shape[0], p.B.shape[0]
@@ -748,6 +765,85 @@ def f1_probe(serac, synth, torch, np, reps: int = 7) -> int:
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+# Exhaustive image sets (images, descriptors per image) for --strips, and the
+# settings compared: the library's test hook SERAC_TEST_STRIP_PAIRS (read at
+# the device's set-up, hence one child process per setting) forces pairs
+# one by one (1) or strips of up to 16 pairs; unset, the library chooses.
+STRIP_SETS = [(200, 512), (128, 1024), (96, 2048), (64, 4096), (48, 8192), (40, 10400)]
+STRIP_SETTINGS = [("per_pair", "1"), ("strips_16", "16"), ("library", None)]
+
+
+def strips_child(serac, synth, torch, np, reps: int) -> int:
+    """One setting: tile-kernel time (HIP events on its dispatch) and call
+    time per pair for each image set, and a digest of all its lists."""
+    out = {}
+    for ni, nd in STRIP_SETS:
+        bt = synth.image_set(ni, nd, 0.15, 3, 0)
+        imgs = [torch.from_numpy(x).to("cuda:0") for x in bt.images]
+        bp = bt.pairs.tolist()
+        res = serac.match_pairs(imgs, bp)          # warm-up: workspace, staging
+        torch.cuda.synchronize()
+        tile, wall = [], []
+        for _ in range(reps):
+            serac.profile_start(1, 1)
+            t0 = time.perf_counter()
+            res = serac.match_pairs(imgs, bp)
+            torch.cuda.synchronize()
+            wall.append(time.perf_counter() - t0)
+            _, n, ms, name = serac.profile_stop()
+            tile.append(ms[0] * 1e3)
+        h = hashlib.sha256()
+        for r in res:
+            h.update(r.cpu().numpy().astype(np.uint32).tobytes())
+        out[f"{ni}x{nd}"] = {"pairs": len(bp), "tile_kernel": name,
+                             "tile_us_median": round(float(np.median(tile)), 3),
+                             "call_us_per_pair_median": round(float(np.median(wall)) * 1e6 / len(bp), 3),
+                             "lists_sha256": h.hexdigest()}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def strips_compare(reps: int = 7) -> int:
+    """Cross-pair reuse of A in a batch (strips, serac_tiles_strip) against
+    the per-pair sweep (serac_tiles_many) on exhaustive image sets of 512 to
+    10400 descriptors per image, each setting in a child process; the lists
+    must be identical under every setting."""
+    runs = {}
+    for label, m in STRIP_SETTINGS:
+        env = {k: v for k, v in os.environ.items() if k != "SERAC_TEST_STRIP_PAIRS"}
+        if m is not None:
+            env["SERAC_TEST_STRIP_PAIRS"] = m
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--strips-child", str(reps)],
+                           env=env, capture_output=True, text=True, timeout=900)
+        if r.returncode != 0:
+            print(r.stderr[-3000:], file=sys.stderr)
+            return 1
+        runs[label] = json.loads(r.stdout.strip().splitlines()[-1])
+        print(f"[strips] {label} done", file=sys.stderr, flush=True)
+    sets = {}
+    same = True
+    for ni, nd in STRIP_SETS:
+        key = f"{ni}x{nd}"
+        row = {label: runs[label][key] for label, _ in STRIP_SETTINGS}
+        digests = {v["lists_sha256"] for v in row.values()}
+        same = same and len(digests) == 1
+        base = row["per_pair"]["tile_us_median"]
+        sets[key] = {
+            "pairs": row["per_pair"]["pairs"],
+            "chunks_per_pair": -(-nd // 256),
+            "tile_us": {label: v["tile_us_median"] for label, v in row.items()},
+            "strips_16_vs_per_pair": round(row["strips_16"]["tile_us_median"] / base - 1.0, 4),
+            "library_kernel": row["library"]["tile_kernel"],
+            "call_us_per_pair": {label: v["call_us_per_pair_median"] for label, v in row.items()},
+            "identical_lists": len(digests) == 1,
+        }
+    line = {"metric": "tile-kernel time of exhaustive image sets, strips of pairs sharing A vs "
+                      "pairs one by one", "unit": "us per call (median)", "reps": reps,
+            "n_gpus": 1, "sets": sets, "identical_lists": same}
+    print(json.dumps(line), flush=True)
+    return 0 if same else 1
 
 
 if __name__ == "__main__":

@@ -220,6 +220,10 @@ int serac_match_pair_noalloc(const uint8_t *descA, int32_t nA, const uint8_t *de
  *   out_matches host array [num_pairs]; out_matches[p] receives pair p's
  *             matches (capacity >= n[pairs[p].a], or the cap if smaller).
  * Every pair gets exactly the result serac_match_pair would give it.
+ * Pairs that share their first image may be swept together (cross-pair
+ * reuse of that image's rows, used where the second images are small, up
+ * to 2048 descriptors on average, and the batch is large enough to keep
+ * the device busy); this changes no result, only the kernel that runs.
  * Asynchronous on params->stream like the other entry points: the host
  * arrays are read before the call returns (they may be released at once);
  * the library copies what the device needs through pinned memory of its

@@ -65,6 +65,12 @@
 //     own acos and trusts it only where a bracket measured against the
 //     table at set-up settles the decision.  The ratio test is one IEEE
 //     multiply and compare.
+//   * In a batch of many pairs with small second images, the pairs that
+//     share their first image are swept in strips: one workgroup keeps a row
+//     block of that image in registers and runs through the second images
+//     of up to 16 pairs as one stream of chunks, its reductions segmented
+//     at the pairs' boundaries, so each pair after the first skips the wait
+//     for its first chunk.
 //   * Variants: symmetric column gates run the sweep of the swapped pair as
 //     well and compare each row's best column's accepted row; the match cap
 //     takes the first descriptors of each set; an unfused comparison arm
@@ -90,6 +96,8 @@
 #include <atomic>
 #include <new>
 #include <type_traits>
+#include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "serac.h"
@@ -115,6 +123,7 @@ constexpr int PLANE_BYTES = CHUNK * 16; // one 16-byte part of every column
 constexpr int GROUP_MAX = 16384;        // columns per workgroup: 512 tiles (the keys' 9-bit index)
 constexpr int MAX_GCH = GROUP_MAX / CHUNK;
 constexpr int COL_RING = 8;             // chunks of column maxima a workgroup keeps in LDS
+constexpr int STRIP_MAX_SEG = 16;       // pairs one workgroup of a strip sweeps (see serac_tiles_strip)
 constexpr int SCR_ROW = 33;              // lane-merge scratch: 32 entries per row plus one of padding
 constexpr int SCR_WAVE = WAVE_ROWS * SCR_ROW;   // entries per wave (8448 bytes)
 // LDS chunk buffer stride: a chunk plus 1 KiB, so that a buffer the chunks no
@@ -182,6 +191,15 @@ struct Job {
     unsigned long long *status;  // [ceil(nA / 256)] finishing hand-off (zero before the finish)
     serac_match *out;        // [>= nA]
     int32_t *count;          // 1
+};
+
+// What a strip's sweep needs of one of its pairs (see serac_tiles_strip).
+struct SegRef {
+    const uint8_t *Bp;
+    const uint32_t *P;
+    unsigned long long *cbest;
+    unsigned long long *rslot;
+    int32_t nB, nBC;
 };
 
 struct Gate {
@@ -319,6 +337,17 @@ __device__ __forceinline__ void lds_barrier()
 }
 
 typedef __attribute__((address_space(3))) void *lds_void_ptr;
+
+// The lane's index in its wave, computed where it is used: volatile, so
+// that the compiler neither hoists it nor keeps an address derived from it
+// live across a loop (for blocks that run rarely inside a register-bound
+// loop).
+__device__ __forceinline__ int lane_here()
+{
+    int id;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(id));
+    return id;
+}
 
 // 16 bytes through a global-address-space pointer: a generic pointer that
 // may point at a __device__ array (the zero descriptor) would otherwise be
@@ -470,11 +499,16 @@ __device__ __forceinline__ int wg_index(uint32_t x, WgOrder o, uint32_t n)
     return (int)((o.a * x + o.b) % n);
 }
 
-template <bool COLS, bool FUSED, bool NARROW>
-__device__ __forceinline__ void tiles_body(const Job &J, int u)
+template <bool COLS, bool FUSED, bool NARROW, bool STRIP = false>
+__device__ __forceinline__ void tiles_body(const Job &J, int u, const Job *__restrict__ jobs = nullptr,
+                                           const int32_t *__restrict__ segJob = nullptr,
+                                           int nseg = 1)
 {
-    // chunk buffers (operand planes), and for a fused sweep the raw chunk
-    __shared__ __attribute__((aligned(16))) uint8_t sB[(FUSED ? 3 : 2) * BUF_BYTES];
+    static_assert(!(STRIP && FUSED), "a strip sweeps prepared sets");
+    // chunk buffers (operand planes), and for a fused sweep the raw chunk;
+    // for a strip, its tables of chunks and of segments after them
+    constexpr int STRIP_TABLE = STRIP ? 4 * STRIP_MAX_SEG * MAX_GCH + sizeof(SegRef) * STRIP_MAX_SEG : 0;
+    __shared__ __attribute__((aligned(16))) uint8_t sB[(FUSED ? 3 : 2) * BUF_BYTES + STRIP_TABLE];
     __shared__ __attribute__((aligned(16))) uint32_t sP[2 * CHUNK];
     __shared__ uint32_t sCol[COLS ? COL_RING * CHUNK : 1];   // ring of chunks: chunk c at c % 8
     // lane-merge scratch, 8448 bytes per wave; a fused sweep merges in the LDS
@@ -483,12 +517,81 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     __shared__ __attribute__((aligned(16))) int32_t sRT[FUSED ? BLOCK_ROWS : 1];
     uint8_t *const sRaw = sB + 2 * BUF_BYTES;
 
+    // a strip's stream of chunks (segment << 8 | chunk inside it) and what
+    // the sweep needs of each segment's pair
+    int32_t *const sChunk = reinterpret_cast<int32_t *>(sB + 2 * BUF_BYTES);
+    SegRef *const sSeg =
+        reinterpret_cast<SegRef *>(sB + 2 * BUF_BYTES + 4 * STRIP_MAX_SEG * MAX_GCH);
+
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, h = lane >> 5;
-    const int rb = u % J.nRB, cg = u / J.nRB;
+    const int rb = STRIP ? u : u % J.nRB, cg = STRIP ? 0 : u / J.nRB;
     const int c0 = cg * J.gch;
-    const int nch = min(J.gch, J.nBC - c0);
+    const int nch = [&]() {
+        if constexpr (STRIP) {
+            // every segment is one pair's whole B (one column group), so the
+            // stream has sum(nBC) chunks; the table is read after the
+            // barrier that ends the prologue (chunk 0 is segment 0's chunk 0)
+            int start = 0;
+            for (int s = 0; s < nseg; ++s) {
+                const Job &Js = jobs[segJob[s]];
+                const int m = Js.nBC;
+                for (int k = tid; k < m; k += TILE_THREADS)
+                    sChunk[start + k] = (s << 8) | k;
+                if (tid == 0)
+                    sSeg[s] = SegRef{Js.Bp, Js.P, Js.cbest, Js.rslot, Js.nB, Js.nBC};
+                start += m;
+            }
+            return start;
+        } else {
+            return min(J.gch, J.nBC - c0);
+        }
+    }();
+    // a segment's entry, read at a uniform LDS address into scalars
+    auto seg_ref = [&](int s) {
+        SegRef r;
+        const uint64_t *q = reinterpret_cast<const uint64_t *>(sSeg + s);
+        auto u64 = [](uint64_t v) {
+            return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v) |
+                   ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32);
+        };
+        r.Bp = reinterpret_cast<const uint8_t *>(u64(q[0]));
+        r.P = reinterpret_cast<const uint32_t *>(u64(q[1]));
+        r.cbest = reinterpret_cast<unsigned long long *>(u64(q[2]));
+        r.rslot = reinterpret_cast<unsigned long long *>(u64(q[3]));
+        r.nB = __builtin_amdgcn_readfirstlane(sSeg[s].nB);
+        r.nBC = __builtin_amdgcn_readfirstlane(sSeg[s].nBC);
+        return r;
+    };
+    // STRIP: a position in the stream of chunks (segment, chunk inside it,
+    // the segment's chunk count), kept in scalars.  next() moves it on by
+    // one chunk and reads the segment table, an LDS read the wave has to
+    // wait for together with all its LDS traffic in flight, only when it
+    // enters a new segment (once per pair, not once per chunk); it returns
+    // whether it did.
+    struct Pos {
+        int s, lc, nbc;
+    };
+    auto next = [&](Pos &p) {
+        if (++p.lc < p.nbc)
+            return false;
+        p.lc = 0;
+        if (++p.s < nseg)
+            p.nbc = __builtin_amdgcn_readfirstlane(sSeg[p.s].nBC);
+        return true;
+    };
+    // segment and chunk (inside its column group) of stream chunk c
+    auto chunk_at = [&](int c, int &s, int &lc) {
+        if constexpr (STRIP) {
+            const int v = __builtin_amdgcn_readfirstlane(sChunk[c]);
+            s = v >> 8;
+            lc = v & 255;
+        } else {
+            s = 0;
+            lc = c0 + c;
+        }
+    };
 
     // ---- fused sweep: raw chunk copy (contiguous, like the chunk itself) and
     // its conversion.  Each wave converts only bytes it copied itself (no
@@ -593,28 +696,68 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
 
     // ---- column maxima of chunk cc raised into the global column bests,
     // column k
-    auto flush_col = [&](int cc, int k) {
-        const int col = (c0 + cc) * CHUNK + k;
+    // (the column bests, first column and width of the pair chunk cc
+    // belongs to: the job's, or for a strip its segment's)
+    struct FlushRef {
+        unsigned long long *cbest;
+        int col0, nB;
+    };
+    auto flush_ref = [&](int cc) {
+        if constexpr (STRIP) {
+            int s, lc;
+            chunk_at(cc, s, lc);
+            const SegRef r = seg_ref(s);
+            return FlushRef{r.cbest, lc * CHUNK, r.nB};
+        } else {
+            return FlushRef{J.cbest, (c0 + cc) * CHUNK, J.nB};
+        }
+    };
+    auto flush_col = [&](const FlushRef &f, int cc, int k) {
+        const int col = f.col0 + k;
         const uint32_t key = sCol[(cc & (COL_RING - 1)) * CHUNK + k];
-        if (col < J.nB && (key >> 9) > 0u) {
+        if (col < f.nB && (key >> 9) > 0u) {
             const uint32_t slice = (uint32_t)(rb * (BLOCK_ROWS / SLICE) + 511 - (int)(key & 511u));
             if constexpr (NARROW)
-                atomicMax(reinterpret_cast<uint32_t *>(J.cbest) + col, (key & ~511u) | (511u - slice));
+                atomicMax(reinterpret_cast<uint32_t *>(f.cbest) + col, (key & ~511u) | (511u - slice));
             else
-                atomicMax(J.cbest + col,
+                atomicMax(f.cbest + col,
                           ((unsigned long long)(key >> 9) << 32) | (0xFFFFFFFFu - slice));
         }
     };
 
     // ---- chunk staging of prepared sets: 8 + (wave 0) 1 loads per thread
+    // STRIP: the chunk the next stage() copies (segment 0's first chunk
+    // to begin with, from the job itself) and its segment's operands
+    Pos fpos{0, 0, J.nBC};
+    const uint8_t *fB = J.Bp;
+    const uint32_t *fP = J.P;
     auto stage = [&](int c, int buf) {
-        const uint8_t *src = J.Bp + (size_t)(c0 + c) * CHUNK_BYTES + tid * 16;
         uint8_t *dst = sB + buf * BUF_BYTES + w * 1024;
+        if constexpr (STRIP) {
+            // uniform bases plus fixed lane offsets
+            const uint8_t *base = fB + (size_t)fpos.lc * CHUNK_BYTES;
 #pragma unroll
-        for (int k = 0; k < CHUNK_BYTES / (TILE_THREADS * 16); ++k)
-            load_lds16(src + k * (TILE_THREADS * 16), dst + k * (TILE_THREADS * 16));
-        if (w == 0)
-            load_lds16(J.P + (size_t)(c0 + c) * CHUNK + lane * 4, sP + buf * CHUNK);
+            for (int k = 0; k < CHUNK_BYTES / (TILE_THREADS * 16); ++k)
+                load_lds16(base + k * (TILE_THREADS * 16), (uint32_t)tid * 16u,
+                           dst + k * (TILE_THREADS * 16));
+            if (w == 0)                      // 16 bytes (four addends) per lane
+                load_lds16(fP + (size_t)fpos.lc * CHUNK, (uint32_t)lane_here() * 16u,
+                           sP + buf * CHUNK);
+            // on to the next chunk (chunk 0's successor is set up after the
+            // barrier that makes the tables readable)
+            if (c > 0 && next(fpos) && fpos.s < nseg) {
+                const SegRef r = seg_ref(fpos.s);
+                fB = r.Bp;
+                fP = r.P;
+            }
+        } else {
+            const uint8_t *src = J.Bp + (size_t)(c0 + c) * CHUNK_BYTES + tid * 16;
+#pragma unroll
+            for (int k = 0; k < CHUNK_BYTES / (TILE_THREADS * 16); ++k)
+                load_lds16(src + k * (TILE_THREADS * 16), dst + k * (TILE_THREADS * 16));
+            if (w == 0)
+                load_lds16(J.P + (size_t)(c0 + c) * CHUNK + lane * 4, sP + buf * CHUNK);
+        }
     };
     if (!FUSED)
         stage(0, 0);
@@ -629,6 +772,16 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
             fetch_raw(1);                    // after the read-back (the plane stores use it)
     }
     __syncthreads();
+    if constexpr (STRIP) {
+        if (nch > 1) {
+            int s1, lc1;
+            chunk_at(1, s1, lc1);
+            const SegRef r = seg_ref(s1);
+            fpos = Pos{s1, lc1, r.nBC};
+            fB = r.Bp;
+            fP = r.P;
+        }
+    }
     if (!FUSED && nch > 1)
         stage(1, 1);                         // needed one chunk from now
 
@@ -709,6 +862,105 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
     // scheduled among themselves.
     auto step_end = [&]() { __builtin_amdgcn_sched_barrier(0); };
 
+    // ---- merge the 32 lanes that share each row, through this wave's own
+    // LDS scratch (no barrier: only this wave writes and reads it): lane pair
+    // (q, q + 32) merges the entries of source lanes 0..15 and 16..31 of row
+    // q pairwise in a four-level tree (dependency depth 4 instead of a
+    // 16-step chain), the lower source lane first in every pair, so on a
+    // key tie (same score, same tile) the lowest lane, which is the lowest
+    // column, stays.
+    // Entry e of row r sits at 33*r + e (rows padded by one entry): the
+    // stores of one row and the loads of one entry from 32 rows both fall on
+    // distinct banks, and every access is a fixed offset from a per-lane
+    // base.  A fused sweep uses the buffers its chunks left free (every wave
+    // is past the last chunk barrier): the buffer of chunk nch-2 for waves
+    // 0..3, the raw copy for waves 4..7.
+    // STRIP: also at every segment boundary, for the pair the segment ended
+    // (a fused sweep never has one); there, inside the loop, the 16 entries
+    // are merged in a chain in lane order instead (the same keys and the
+    // same lowest lane on a tie, with fewer registers live beside the
+    // accumulators).
+    auto publish = [&](unsigned long long *rslot, int cgs, int c0s, auto chain) {
+        // the lane's row and half; inside the loop taken afresh from the
+        // lane id (volatile, so that the compiler keeps this block's
+        // addresses out of the registers live across the whole loop)
+        int nl = n, hl = h;
+        if constexpr (decltype(chain)::value) {
+            const int id = lane_here();
+            nl = id & 31;
+            hl = id >> 5;
+        }
+        uint2 *scr;
+        if (FUSED)
+            scr = reinterpret_cast<uint2 *>((w < 4 ? sB + (nch & 1) * BUF_BYTES : sRaw)) +
+                  (w & 3) * SCR_WAVE;
+        else
+            scr = sScr + w * SCR_WAVE;
+        // Row 16h + rr, entry n is at wb + SCR_ROW*rr, and row n, entry 16h + k
+        // at rb + k.
+        uint2 *const wb = scr + SCR_ROW * 16 * hl + nl;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+            wb[SCR_ROW * rr] = make_uint2(b1[rr], b2[rr]);
+        const uint2 *const rbp = scr + SCR_ROW * nl + 16 * hl;
+        uint32_t K1, K2;
+        int L1;                                              // source lane (column in the tile)
+        if constexpr (decltype(chain)::value) {
+            K1 = 0u;
+            K2 = 0u;
+            int k1 = 0;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const uint2 e = rbp[k];
+                k1 = e.x > K1 ? k : k1;
+                K2 = umax3(min(K1, e.x), K2, e.y);
+                K1 = max(K1, e.x);
+            }
+            L1 = 16 * hl + k1;
+        } else {
+            uint32_t t1[16], t2[16];
+            int tl[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const uint2 e = rbp[k];
+                t1[k] = e.x;
+                t2[k] = e.y;
+                tl[k] = k;
+            }
+#pragma unroll
+            for (int s = 1; s < 16; s *= 2) {
+#pragma unroll
+                for (int k = 0; k < 16; k += 2 * s) {
+                    const uint32_t a1 = t1[k], b1 = t1[k + s];
+                    tl[k] = b1 > a1 ? tl[k + s] : tl[k];
+                    t2[k] = umax3(min(a1, b1), t2[k], t2[k + s]);
+                    t1[k] = max(a1, b1);
+                }
+            }
+            K1 = t1[0];
+            K2 = t2[0];
+            L1 = 16 * hl + tl[0];
+        }
+        {
+            // lane half 0 holds the lower source lanes: it keeps its own on a tie
+            const uint32_t o1 = __shfl_xor(K1, 32), o2 = __shfl_xor(K2, 32);
+            const int oL = __shfl_xor(L1, 32);
+            L1 = (o1 > K1 || (hl == 1 && o1 == K1)) ? oL : L1;
+            K2 = umax3(min(K1, o1), K2, o2);
+            K1 = max(K1, o1);
+        }
+        // publish this row block's top-2 over the workgroup's columns as one
+        // packed slot per (row, column group); the finishing kernel merges the
+        // groups
+        const int row = rb * BLOCK_ROWS + w * WAVE_ROWS + nl;
+        if (hl == 0 && row < J.nA) {
+            const uint32_t S1 = K1 >> 9, S2 = K2 >> 9;
+            const int window = (c0s * CHUNK) & ~(GROUP_MAX - 1);
+            const uint32_t col = (uint32_t)(window + 32 * (511 - (int)(K1 & 511u)) + L1);
+            rslot[(size_t)cgs * J.nA + row] = pack_slot(S1, col, S2);
+        }
+    };
+
     // chunk c: pairs 1..3 of the chunk and pair 0 of the next one (pair 0
     // of chunk 0 is issued before the loop)
     // Issue priority of the two waves sharing a SIMD: with equal priorities
@@ -724,8 +976,37 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
         else
             __builtin_amdgcn_s_setprio(0);
     };
-    auto chunk = [&](int c) {
+    // STRIP: positions of the chunk being swept and of the chunk whose
+    // column maxima are flushed next, with that chunk's column bests
+    Pos cpos{0, 0, J.nBC}, xpos{0, 0, J.nBC};
+    FlushRef xref{J.cbest, 0, J.nB};
+    // `when`: whether chunk c is the last, known at compile time in a strip
+    // (its last chunk is peeled off the loop: with a branch on it in the
+    // loop body the compiler hoisted the last pair's key construction, common
+    // to both arms, above the branch, which then waited for the step's MFMAs
+    // before the chunk barrier), tested at run time otherwise
+    auto chunk = [&](int c, auto when) {
         const int buf = c & 1;
+        if constexpr (STRIP) {
+            // chunk c starts a new segment: the previous pair's rows are
+            // complete (a chunk's last pair closes the deferred fold), so
+            // they are published and the running top-2 starts again.  Done
+            // before the step's MFMAs are issued, so that the step stays one
+            // block in which the compiler interleaves them with the
+            // epilogue.
+            if (c > 0 && cpos.lc == 0) {
+                publish(seg_ref(cpos.s - 1).rslot, 0, 0, std::true_type{});
+                // a fresh opaque zero (see above), not one kept live across
+                // the loop
+                uint32_t z;
+                asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    b1[x] = z;
+                    b2[x] = z;
+                }
+            }
+        }
         turn(1);
         mfma(1);
         epi(0, c, 0, Even{});
@@ -744,8 +1025,20 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
         if (COLS && c >= COL_RING - 1) {
             // chunk c-7's column maxima are final (every wave is past two
             // chunk barriers since); its ring slot is chunk c+1's
-            if (tid < CHUNK) {
-                flush_col(c - (COL_RING - 1), tid);
+            if constexpr (STRIP) {
+                // waves 0..3 (the test on the wave index keeps the flush
+                // position in scalars)
+                if (w < CHUNK / 64) {
+                    flush_col(xref, c - (COL_RING - 1), tid);
+                    sCol[((c + 1) & (COL_RING - 1)) * CHUNK + tid] = 0u;
+                    if (next(xpos) && xpos.s < nseg) {
+                        const SegRef r = seg_ref(xpos.s);
+                        xref = FlushRef{r.cbest, 0, r.nB};
+                    }
+                    xref.col0 = xpos.lc * CHUNK;
+                }
+            } else if (tid < CHUNK) {
+                flush_col(flush_ref(c - (COL_RING - 1)), c - (COL_RING - 1), tid);
                 sCol[((c + 1) & (COL_RING - 1)) * CHUNK + tid] = 0u;
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -759,7 +1052,8 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
         mfma(1);
         epi(0, c, 2, Even{});
         step_end();
-        if (c + 1 < nch) {
+        constexpr int WHEN = decltype(when)::value;   // 0: not last, 1: last, 2: test
+        if (WHEN == 2 ? c + 1 < nch : WHEN == 0) {
             if (!FUSED)
                 wait_vmcnt<0>();             // chunk c+1 landed (this wave's part)
             __syncthreads();                 // ... all parts; chunk c no longer read
@@ -775,92 +1069,44 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u)
         } else {
             epi(1, c, 3, Odd{});
         }
+        if constexpr (STRIP)
+            next(cpos);
     };
 
     frags(0, 0, 0);
     mfma(0);
     frags(0, 1, 1);
     step_end();
-    for (int c = 0; c < nch; ++c)
-        chunk(c);
+    if constexpr (STRIP) {
+        for (int c = 0; c < nch - 1; ++c)
+            chunk(c, std::integral_constant<int, 0>{});
+        chunk(nch - 1, std::integral_constant<int, 1>{});
+    } else {
+        for (int c = 0; c < nch; ++c)
+            chunk(c, std::integral_constant<int, 2>{});
+    }
 
     __builtin_amdgcn_s_setprio(0);
     // ---- column maxima out first: their atomics complete behind the merge
     if (COLS) {
         lds_barrier();                       // every wave's column maxima are in
-        // the chunks still in the ring
+        // the chunks still in the ring (a strip's table read is convergent:
+        // that loop is not unrolled)
+        const uint32_t k0 = (uint32_t)(max(nch - (COL_RING - 1), 0) * CHUNK + tid);
+        if constexpr (STRIP) {
+            for (uint32_t k = k0; k < (uint32_t)(nch * CHUNK); k += TILE_THREADS)
+                flush_col(flush_ref((int)(k / CHUNK)), (int)(k / CHUNK), (int)(k % CHUNK));
+        } else {
 #pragma unroll 2
-        for (uint32_t k = (uint32_t)(max(nch - (COL_RING - 1), 0) * CHUNK + tid);
-             k < (uint32_t)(nch * CHUNK); k += TILE_THREADS)
-            flush_col((int)(k / CHUNK), (int)(k % CHUNK));
-    }
-
-    // ---- merge the 32 lanes that share each row, through this wave's own
-    // LDS scratch (no barrier: only this wave writes and reads it): lane pair
-    // (q, q + 32) merges the entries of source lanes 0..15 and 16..31 of row
-    // q pairwise in a four-level tree (dependency depth 4 instead of a
-    // 16-step chain), the lower source lane first in every pair, so on a
-    // key tie (same score, same tile) the lowest lane, which is the lowest
-    // column, stays.
-    // Entry e of row r sits at 33*r + e (rows padded by one entry): the
-    // stores of one row and the loads of one entry from 32 rows both fall on
-    // distinct banks, and every access is a fixed offset from a per-lane
-    // base.  A fused sweep uses the buffers its chunks left free (every wave
-    // is past the last chunk barrier): the buffer of chunk nch-2 for waves
-    // 0..3, the raw copy for waves 4..7.
-    uint2 *scr;
-    if (FUSED)
-        scr = reinterpret_cast<uint2 *>((w < 4 ? sB + (nch & 1) * BUF_BYTES : sRaw)) +
-              (w & 3) * SCR_WAVE;
-    else
-        scr = sScr + w * SCR_WAVE;
-    // Row 16h + rr, entry n is at wb + SCR_ROW*rr, and row n, entry 16h + k
-    // at rb + k.
-    uint2 *const wb = scr + SCR_ROW * 16 * h + n;
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr)
-        wb[SCR_ROW * rr] = make_uint2(b1[rr], b2[rr]);
-    const uint2 *const rbp = scr + SCR_ROW * n + 16 * h;
-    uint32_t t1[16], t2[16];
-    int tl[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const uint2 e = rbp[k];
-        t1[k] = e.x;
-        t2[k] = e.y;
-        tl[k] = k;
-    }
-#pragma unroll
-    for (int s = 1; s < 16; s *= 2) {
-#pragma unroll
-        for (int k = 0; k < 16; k += 2 * s) {
-            const uint32_t a1 = t1[k], b1 = t1[k + s];
-            tl[k] = b1 > a1 ? tl[k + s] : tl[k];
-            t2[k] = umax3(min(a1, b1), t2[k], t2[k + s]);
-            t1[k] = max(a1, b1);
+            for (uint32_t k = k0; k < (uint32_t)(nch * CHUNK); k += TILE_THREADS)
+                flush_col(flush_ref((int)(k / CHUNK)), (int)(k / CHUNK), (int)(k % CHUNK));
         }
     }
-    uint32_t K1 = t1[0], K2 = t2[0];
-    int L1 = 16 * h + tl[0];                             // source lane (column in the tile)
-    {
-        // lane half 0 holds the lower source lanes: it keeps its own on a tie
-        const uint32_t o1 = __shfl_xor(K1, 32), o2 = __shfl_xor(K2, 32);
-        const int oL = __shfl_xor(L1, 32);
-        L1 = (o1 > K1 || (h == 1 && o1 == K1)) ? oL : L1;
-        K2 = umax3(min(K1, o1), K2, o2);
-        K1 = max(K1, o1);
-    }
-    // publish this row block's top-2 over the workgroup's columns as one
-    // packed slot per (row, column group); the finishing kernel merges the
-    // groups
-    const int row = rb * BLOCK_ROWS + w * WAVE_ROWS + n;
-    if (h == 0 && row < J.nA) {
-        const uint32_t S1 = K1 >> 9, S2 = K2 >> 9;
-        const int window = (c0 * CHUNK) & ~(GROUP_MAX - 1);
-        const uint32_t col = (uint32_t)(window + 32 * (511 - (int)(K1 & 511u)) + L1);
-        J.rslot[(size_t)cg * J.nA + row] = pack_slot(S1, col, S2);
-    }
 
+    if constexpr (STRIP)
+        publish(seg_ref(nseg - 1).rslot, 0, 0, std::false_type{});
+    else
+        publish(J.rslot, cg, c0, std::false_type{});
 }
 
 // NARROW: the column bests take 32 bits (J.cb32; see col_best_at).
@@ -907,6 +1153,41 @@ __global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_many(const Job *_
     if (u >= J.nRB * J.Gc)
         return;
     tiles_body<COLS, false, NARROW>(J, u);
+}
+
+// Cross-pair reuse of a staged row block in a batch (an exhaustive image
+// set matches each image as A against many others).  One workgroup sweeps
+// row block rb of an image against the B sides of up to STRIP_MAX_SEG pairs
+// that share that image as A, as one stream of chunks: the A operands and
+// row terms are loaded once, and the software pipeline runs on across the
+// pairs, the first chunks of the next pair staged while the last ones of
+// the current pair are swept, so only one prologue is paid per strip.  The
+// reductions are segmented at the pairs' boundaries: when a chunk starts a
+// new pair, the finished pair's row top-2 goes through the lane merge into
+// its slots and the running keys start again from zero; column maxima go
+// to the column bests of the pair their chunk belongs to.  Every pair of a
+// strip has its whole B in one column group (at most 16384 columns, the
+// keys' tile index), so its slots and column bests are the same as a
+// single-pair sweep's and the finishing kernel is unchanged.
+//   strips[s] = (first entry in stripJobs, number of pairs), the pairs'
+//   jobs listed in stripJobs, all with the same A; workgroup x sweeps row
+//   block x % rbPerStrip of strip x / rbPerStrip.
+struct StripRef {
+    int32_t first, count;
+};
+
+template <bool COLS, bool NARROW>
+__global__ __launch_bounds__(TILE_THREADS, 2) void serac_tiles_strip(
+    const Job *__restrict__ jobs, const int32_t *__restrict__ stripJobs,
+    const StripRef *__restrict__ strips, int rbPerStrip, WgOrder o, uint32_t blocks)
+{
+    const int x = wg_index(blockIdx.x, o, blocks);
+    const StripRef S = strips[x / rbPerStrip];
+    const int rb = x % rbPerStrip;
+    const Job J = jobs[stripJobs[S.first]];
+    if (rb >= J.nRB)
+        return;
+    tiles_body<COLS, false, NARROW, true>(J, rb, jobs, stripJobs + S.first, S.count);
 }
 
 // Exact inner product of two descriptors (used only to settle column ties
@@ -1580,6 +1861,14 @@ double angle_slack(const double *table)
 
 int fixed_setup(int dev);
 
+// Test hook SERAC_TEST_STRIP_PAIRS=<m> (read at a device's set-up): 1 turns
+// a batch's strips off; 2..STRIP_MAX_SEG puts up to m pairs in each strip
+// whatever number of workgroups that leaves (see make_strips).
+std::atomic<int> g_strip_pairs{0};
+constexpr int STRIP_ROUNDS = 8;         // workgroups per compute unit a strip plan keeps
+constexpr int STRIP_MAX_CHUNKS = 8;     // mean chunks of B per pair up to which strips pay
+
+
 // Test hook SERAC_TEST_WG_ORDER=<seed> (read at a device's set-up; 0 or
 // unset: the library's own order): the tile kernels sweep their tiles in a
 // permuted workgroup order (see WgOrder).
@@ -1638,6 +1927,12 @@ int device_setup(Device **out)
             const unsigned long v = std::strtoul(e, &end, 10);
             if (end != e && v <= 0xFFFFFFFFul)
                 g_order_seed.store((uint32_t)v, std::memory_order_relaxed);
+        }
+        if (const char *e = std::getenv("SERAC_TEST_STRIP_PAIRS")) {
+            char *end = nullptr;
+            const long v = std::strtol(e, &end, 10);
+            if (end != e && v >= 1 && v <= STRIP_MAX_SEG)
+                g_strip_pairs.store((int)v, std::memory_order_relaxed);
         }
         // angle of every attainable clamped score, with the C library's acos
         std::vector<double> t(NORM2 + 1);
@@ -1969,6 +2264,91 @@ Plan make_plan(int nA, int nB, long long target, int cus = 0)
     p.acc = align256((size_t)nB * 8) + align256(gates * 8);
     p.scratch = align256((size_t)nA * 4) + align256((size_t)p.Gc * nA * 8);
     return p;
+}
+
+// Strips of a batch (serac_tiles_strip): the jobs of each A image, in job
+// order, cut into runs of nearly equal length of at most m jobs.  Used when
+// every job's B is one column group and the pairs' B sides average at most
+// STRIP_MAX_CHUNKS chunks; m is the largest value up to STRIP_MAX_SEG that
+// still leaves STRIP_ROUNDS workgroups per compute unit, and at m = 1 (a
+// strip per pair, nothing to reuse) the batch keeps serac_tiles_many.
+// Strips save each pair after a strip's first the latency of its first
+// chunk and the workgroup's start and drain, but not its lane merge or
+// column flush: measured on exhaustive image sets, the tile kernel took
+// 13.5% less time with 512-descriptor images (2 chunks per pair), 8.6% less
+// with 1024, 3% less with 2048, and 1-3% more with 4096 and 10400, about
+// the same with 8192 (one MI355X; strips of up to 16 pairs).  Strips with
+// more chunks come first, so that the last workgroups to start are the
+// short ones.  Returns the row blocks per strip (the grid's stride), or 0
+// for no strips.
+int make_strips(const std::vector<int> &jobA, const std::vector<Plan> &plans, int cus,
+                std::vector<int32_t> &stripJobs, std::vector<StripRef> &strips)
+{
+    stripJobs.clear();
+    strips.clear();
+    const int njobs = (int)jobA.size();
+    if (njobs < 2)
+        return 0;
+    for (const Plan &p : plans)
+        if (p.Gc != 1)
+            return 0;
+    // jobs per A image, images in order of their first job
+    std::vector<std::vector<int>> runs;
+    std::unordered_map<int, int> at;
+    for (int k = 0; k < njobs; ++k) {
+        auto it = at.find(jobA[k]);
+        if (it == at.end()) {
+            at.emplace(jobA[k], (int)runs.size());
+            runs.push_back({k});
+        } else {
+            runs[it->second].push_back(k);
+        }
+    }
+    auto workgroups = [&](int m) {
+        long long wg = 0;
+        for (const auto &r : runs)
+            wg += (long long)(((int)r.size() + m - 1) / m) * plans[r[0]].nRB;
+        return wg;
+    };
+    int m = g_strip_pairs.load(std::memory_order_relaxed);
+    if (m == 0) {
+        long long chunks = 0;
+        for (const Plan &p : plans)
+            chunks += p.nBC;
+        if (chunks > (long long)STRIP_MAX_CHUNKS * njobs)
+            return 0;
+        m = 1;
+        for (int t = STRIP_MAX_SEG; t >= 2; --t)
+            if (workgroups(t) >= (long long)STRIP_ROUNDS * cus) {
+                m = t;
+                break;
+            }
+    }
+    if (m < 2)
+        return 0;
+    std::vector<std::pair<long long, StripRef>> order;
+    int rbPerStrip = 0;
+    for (const auto &r : runs) {
+        const int c = (int)r.size(), k = (c + m - 1) / m;
+        int pos = 0;
+        for (int q = 0; q < k; ++q) {
+            const int len = c / k + (q < c % k ? 1 : 0);
+            long long chunks = 0;
+            StripRef S{(int32_t)stripJobs.size(), len};
+            for (int e = 0; e < len; ++e) {
+                stripJobs.push_back(r[pos + e]);
+                chunks += plans[r[pos + e]].nBC;
+            }
+            pos += len;
+            order.push_back({chunks, S});
+        }
+        rbPerStrip = std::max(rbPerStrip, plans[r[0]].nRB);
+    }
+    std::stable_sort(order.begin(), order.end(),
+                     [](const auto &a, const auto &b) { return a.first > b.first; });
+    for (const auto &o : order)
+        strips.push_back(o.second);
+    return rbPerStrip;
 }
 
 int round_up(int n, int m) { return (n + m - 1) / m * m; }
@@ -2482,22 +2862,37 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
             b = k < nlive ? pr.b : pr.a;
         };
         const long long target = njobs ? std::max(1LL, (4LL * d->cus + njobs - 1) / njobs) : 1;
-        std::vector<Plan> plans(njobs);
+        std::vector<Plan> plans(njobs), whole(njobs);
+        std::vector<int> jobA(njobs);
+        for (int k = 0; k < njobs; ++k) {
+            int b;
+            job_sets(k, jobA[k], b);
+            plans[k] = make_plan(nc[jobA[k]], nc[b], target);
+            whole[k] = make_plan(nc[jobA[k]], nc[b], 1);   // B in as few column groups as fit
+        }
+        // Strips (cross-pair reuse of A) take every pair's B in one column
+        // group; when they are used, those plans replace the ones that split
+        // columns for parallelism.
+        std::vector<int32_t> stripJobs;
+        std::vector<StripRef> strips;
+        const int rbPerStrip = make_strips(jobA, whole, d->cus, stripJobs, strips);
+        if (rbPerStrip > 0)
+            plans.swap(whole);
         size_t acc_bytes = 0, res_bytes = 0;
         int unitsPerJob = 1, gatePerJob = 1;
         for (int k = 0; k < njobs; ++k) {
-            int a, b;
-            job_sets(k, a, b);
-            plans[k] = make_plan(nc[a], nc[b], target);
             acc_bytes += plans[k].acc;
             res_bytes += plans[k].scratch;
             unitsPerJob = std::max(unitsPerJob, plans[k].units());
-            gatePerJob = std::max(gatePerJob, (nc[a] + GATE_THREADS - 1) / GATE_THREADS);
+            gatePerJob = std::max(gatePerJob, (nc[jobA[k]] + GATE_THREADS - 1) / GATE_THREADS);
         }
         const size_t jobs_bytes = align256(sizeof(Job) * (size_t)std::max(njobs, 1));
         const size_t prepjobs_bytes = align256(sizeof(PrepJob) * std::max<size_t>(prepped.size(), 1));
         const size_t zero_bytes = align256(sizeof(int32_t *) * zero.size() + 8);
-        const size_t host_bytes = jobs_bytes + prepjobs_bytes + zero_bytes;
+        const size_t sjobs_bytes = align256(sizeof(int32_t) * stripJobs.size() + 8);
+        const size_t strips_bytes = align256(sizeof(StripRef) * strips.size() + 8);
+        const size_t host_bytes = jobs_bytes + prepjobs_bytes + zero_bytes + sjobs_bytes +
+                                  strips_bytes;
         Workspace *w = nullptr;
         std::unique_lock<std::mutex> hold;
         st = get_workspace(stream, acc_bytes, host_bytes + res_bytes + prep_total, &w, hold);
@@ -2538,6 +2933,12 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
             jobs[k].cb32 = narrow ? 1 : 0;
         for (size_t k = 0; k < zero.size(); ++k)
             zp[k] = zero[k];
+        const size_t sjobs_at = jobs_bytes + prepjobs_bytes + zero_bytes;
+        const size_t strips_at = sjobs_at + sjobs_bytes;
+        if (!stripJobs.empty())
+            std::memcpy(host + sjobs_at, stripJobs.data(), sizeof(int32_t) * stripJobs.size());
+        if (!strips.empty())
+            std::memcpy(host + strips_at, strips.data(), sizeof(StripRef) * strips.size());
         hipError_t e = hipMemcpyAsync(w->aux, host, host_bytes, hipMemcpyHostToDevice, stream);
         if (e == hipSuccess)
             e = hipEventRecord(staged, stream);   // the staging buffer is reusable once this has run
@@ -2556,21 +2957,45 @@ int serac_match_pairs(const uint8_t *const *desc, const int32_t *n, int32_t num_
             Gate G = make_gate(d, params);
             const bool cols = params->cross_check && !sym;
             hipEvent_t e0, e1;
-            prof_slot(e0, e1,
-                      !cols    ? "serac_tiles_many<false, false>"
-                      : narrow ? "serac_tiles_many<true, true>"
-                               : "serac_tiles_many<true, false>");
-            const dim3 grid(njobs * unitsPerJob);
-            const WgOrder o = wg_order(grid.x);
-            if (!cols)
-                hipExtLaunchKernelGGL(serac_tiles_many<false, false>, grid, dim3(TILE_THREADS), 0,
-                                      stream, e0, e1, 0, djobs, unitsPerJob, o, grid.x);
-            else if (narrow)
-                hipExtLaunchKernelGGL(serac_tiles_many<true, true>, grid, dim3(TILE_THREADS), 0,
-                                      stream, e0, e1, 0, djobs, unitsPerJob, o, grid.x);
-            else
-                hipExtLaunchKernelGGL(serac_tiles_many<true, false>, grid, dim3(TILE_THREADS), 0,
-                                      stream, e0, e1, 0, djobs, unitsPerJob, o, grid.x);
+            if (rbPerStrip > 0) {
+                // cross-pair reuse of A: strips of pairs sharing their A image
+                prof_slot(e0, e1,
+                          !cols    ? "serac_tiles_strip<false, false>"
+                          : narrow ? "serac_tiles_strip<true, true>"
+                                   : "serac_tiles_strip<true, false>");
+                const int32_t *dsj = reinterpret_cast<const int32_t *>(w->aux + sjobs_at);
+                const StripRef *dst = reinterpret_cast<const StripRef *>(w->aux + strips_at);
+                const dim3 grid((unsigned)strips.size() * rbPerStrip);
+                const WgOrder o = wg_order(grid.x);
+                if (!cols)
+                    hipExtLaunchKernelGGL(serac_tiles_strip<false, false>, grid, dim3(TILE_THREADS),
+                                          0, stream, e0, e1, 0, djobs, dsj, dst, rbPerStrip, o,
+                                          grid.x);
+                else if (narrow)
+                    hipExtLaunchKernelGGL(serac_tiles_strip<true, true>, grid, dim3(TILE_THREADS),
+                                          0, stream, e0, e1, 0, djobs, dsj, dst, rbPerStrip, o,
+                                          grid.x);
+                else
+                    hipExtLaunchKernelGGL(serac_tiles_strip<true, false>, grid, dim3(TILE_THREADS),
+                                          0, stream, e0, e1, 0, djobs, dsj, dst, rbPerStrip, o,
+                                          grid.x);
+            } else {
+                prof_slot(e0, e1,
+                          !cols    ? "serac_tiles_many<false, false>"
+                          : narrow ? "serac_tiles_many<true, true>"
+                                   : "serac_tiles_many<true, false>");
+                const dim3 grid(njobs * unitsPerJob);
+                const WgOrder o = wg_order(grid.x);
+                if (!cols)
+                    hipExtLaunchKernelGGL(serac_tiles_many<false, false>, grid, dim3(TILE_THREADS),
+                                          0, stream, e0, e1, 0, djobs, unitsPerJob, o, grid.x);
+                else if (narrow)
+                    hipExtLaunchKernelGGL(serac_tiles_many<true, true>, grid, dim3(TILE_THREADS), 0,
+                                          stream, e0, e1, 0, djobs, unitsPerJob, o, grid.x);
+                else
+                    hipExtLaunchKernelGGL(serac_tiles_many<true, false>, grid, dim3(TILE_THREADS),
+                                          0, stream, e0, e1, 0, djobs, unitsPerJob, o, grid.x);
+            }
             if (sym) {
                 G.cross_check = 0;
                 serac_finish_many_sym<SYM_COLUMNS><<<nlive * gatePerJob, GATE_THREADS, 0, stream>>>(
