@@ -518,7 +518,9 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u, const Job *__res
     uint8_t *const sRaw = sB + 2 * BUF_BYTES;
 
     // a strip's stream of chunks (segment << 8 | chunk inside it) and what
-    // the sweep needs of each segment's pair
+    // the sweep needs of each segment's pair, in the space past the two
+    // chunk buffers that a fused sweep uses for its raw chunk (a strip is
+    // never fused)
     int32_t *const sChunk = reinterpret_cast<int32_t *>(sB + 2 * BUF_BYTES);
     SegRef *const sSeg =
         reinterpret_cast<SegRef *>(sB + 2 * BUF_BYTES + 4 * STRIP_MAX_SEG * MAX_GCH);
@@ -695,9 +697,9 @@ __device__ __forceinline__ void tiles_body(const Job &J, int u, const Job *__res
     }
 
     // ---- column maxima of chunk cc raised into the global column bests,
-    // column k
-    // (the column bests, first column and width of the pair chunk cc
-    // belongs to: the job's, or for a strip its segment's)
+    // column k.  A FlushRef holds the column bests, first column and width
+    // of the pair chunk cc belongs to: the job's, or for a strip its
+    // segment's.
     struct FlushRef {
         unsigned long long *cbest;
         int col0, nB;
