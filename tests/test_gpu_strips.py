@@ -12,8 +12,9 @@ list must equal the oracle's, with and without the cross-check, with
 symmetric gates and with the match cap; the profiler hook names the tile
 kernel that ran, so the test knows the strips were used.  A batch with a B
 side wider than one column group keeps the per-pair sweep, and without the
-hook the library picks strips for a large set of small images.  Through the
-C ABI.
+hook the library picks strips for a large set of small images.  The host
+pipeline, whose stages are batches, is checked under forced strips too.
+Through the C ABI.
 """
 import json
 import os
@@ -56,10 +57,14 @@ for prm in cfg["params"]:
     torch.cuda.synchronize()
     _, n, _, kname = serac.profile_stop()
     assert kname.startswith(cfg["kernel"]), (kname, cfg["kernel"])
+    host = serac.match_pairs_host(dev, pairs, pairs_per_stage=cfg["stage"], **prm) \
+        if cfg.get("stage") else None
     for q, (a, b) in enumerate(pairs):
         want = oracle.match_pair(imgs[a], imgs[b], **prm)
         got = res[q].cpu().numpy().astype(np.uint32)
         assert got.tobytes() == want.tobytes(), (prm, a, b, len(got), len(want))
+        if host is not None:
+            assert host[q].tobytes() == want.tobytes(), ("host", prm, a, b)
     print("ok", kname, len(pairs), json.dumps(prm), flush=True)
 """
 
@@ -72,8 +77,10 @@ PARAMS = [dict(max_ratio=0.8, max_distance=1e9, cross_check=True),
           dict(max_ratio=0.8, max_distance=1e9, cross_check=True, max_features=1000)]
 
 CASES = {
+    # the host pipeline as well, in stages of 7 pairs (each stage a batch
+    # swept in strips)
     "m2_mixed": (dict(SERAC_TEST_STRIP_PAIRS="2"),
-                 dict(seed=1, sizes=MIXED, params=PARAMS, kernel="serac_tiles_strip")),
+                 dict(seed=1, sizes=MIXED, params=PARAMS, kernel="serac_tiles_strip", stage=7)),
     "m3_wide_order": (dict(SERAC_TEST_STRIP_PAIRS="3", SERAC_TEST_WG_ORDER="977"),
                       dict(seed=2, sizes=WIDE, params=PARAMS[:2], kernel="serac_tiles_strip")),
     "m16_many": (dict(SERAC_TEST_STRIP_PAIRS="16"),
