@@ -21,6 +21,7 @@ import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 pytestmark = pytest.mark.gpu
@@ -48,8 +49,15 @@ for a in range(len(imgs) - 1):
         src = rng.choice(len(imgs[a]), k, replace=False)
         dst = rng.choice(len(imgs[b]), k, replace=False)
         imgs[b][dst] = synth.noisy(rng, imgs[a][src], 3)
-pairs = [(a, b) for a in range(len(imgs)) for b in range(len(imgs)) if a != b and (a < b or (a + b) % 3 == 0)]
-pairs += [(1, 1), (0, 2)]
+if cfg.get("random_pairs"):
+    # a random pair list: both orders, self pairs and repeats
+    n = len(imgs)
+    pairs = [(int(x), int(y)) for x, y in rng.integers(0, n, size=(cfg["random_pairs"], 2))]
+    pairs += pairs[:5]
+else:
+    pairs = [(a, b) for a in range(len(imgs)) for b in range(len(imgs))
+             if a != b and (a < b or (a + b) % 3 == 0)]
+    pairs += [(1, 1), (0, 2)]
 dev = [torch.from_numpy(np.ascontiguousarray(x)).to("cuda:0") for x in imgs]
 for prm in cfg["params"]:
     serac.profile_start(4)
@@ -91,6 +99,16 @@ CASES = {
     # images (80 x 512 descriptors, about 5300 pairs)
     "default_small_images": ({}, dict(seed=6, sizes=[512] * 80, params=PARAMS[:1] + PARAMS[3:4],
                                       kernel="serac_tiles_strip")),
+    # seeded random sets: sizes 0..3000, a random pair list, random strip
+    # lengths
+    "random_a": (dict(SERAC_TEST_STRIP_PAIRS="5"),
+                 dict(seed=21, sizes=[int(x) for x in
+                                      np.random.default_rng(21).integers(0, 3001, 14)],
+                      random_pairs=90, params=PARAMS[:2], kernel="serac_tiles_strip")),
+    "random_b": (dict(SERAC_TEST_STRIP_PAIRS="11"),
+                 dict(seed=22, sizes=[int(x) for x in
+                                      np.random.default_rng(22).integers(0, 3001, 9)] + [1, 257],
+                      random_pairs=70, params=PARAMS[2:4], kernel="serac_tiles_strip")),
     "off": (dict(SERAC_TEST_STRIP_PAIRS="1"),
             dict(seed=4, sizes=MIXED[:6], params=PARAMS[:1], kernel="serac_tiles_many")),
     "too_wide_for_strips": (dict(SERAC_TEST_STRIP_PAIRS="4"),
